@@ -1,0 +1,317 @@
+"""Python binding of libdsa: torch tensors in, C ABI calls out.
+
+This layer only marshals arguments (shape/dtype checks, output and workspace
+allocation with torch, the current HIP stream); every step of the computation
+runs in libdsa's HIP kernels. There is no fallback: if libdsa.so is missing,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [status {status}]")
+        self.status = status
+
+
+def load():
+    return L.load()
+
+
+def _check(status: int):
+    if status != L.DSA_OK:
+        lib = L.load()
+        name = lib.dsa_status_string(status).decode()
+        msg = lib.dsa_last_error().decode()
+        raise DsaError(status, f"{name}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def abi_version() -> int:
+    return int(L.load().dsa_abi_version())
+
+
+def resolve_pattern(n_layers: int, pattern: Optional[str] = None, freq: int = 0) -> str:
+    """IndexCache pattern resolution through the library (pure host code)."""
+    buf = ctypes.create_string_buffer(max(n_layers, 0) + 1)
+    pat = None if pattern is None else pattern.encode()
+    _check(L.load().dsa_resolve_pattern(int(n_layers), pat, int(freq), buf))
+    return buf.value.decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.DSA_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return L.DSA_FP8_E4M3FN
+    raise TypeError(f"indexer inputs must be bfloat16 or float8_e4m3fn, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def indexer_args(B, n_q, n_k, pos_offset, H, D, topk, dtype_code) -> L.IndexerArgs:
+    a = L.IndexerArgs()
+    a.struct_size = ctypes.sizeof(L.IndexerArgs)
+    a.B, a.n_q, a.n_k, a.q_pos_offset = B, n_q, n_k, pos_offset
+    a.n_heads, a.head_dim, a.topk, a.dtype = H, D, topk, dtype_code
+    return a
+
+
+def attn_args(B, n_q, n_k, pos_offset, H, D, topk, scale) -> L.AttnArgs:
+    a = L.AttnArgs()
+    a.struct_size = ctypes.sizeof(L.AttnArgs)
+    a.B, a.n_q, a.n_k, a.q_pos_offset = B, n_q, n_k, pos_offset
+    a.n_heads, a.head_dim, a.topk, a.scale = H, D, topk, float(scale)
+    return a
+
+
+def indexer_workspace_size(B, n_q, n_k, H, D, topk, dtype_code=L.DSA_BF16, pos_offset=None) -> int:
+    if pos_offset is None:
+        pos_offset = n_k - n_q
+    a = indexer_args(B, n_q, n_k, pos_offset, H, D, topk, dtype_code)
+    n = ctypes.c_size_t(0)
+    _check(L.load().dsa_indexer_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    return int(n.value)
+
+
+def attn_workspace_size(B, n_q, n_k, H, D, topk, pos_offset=None) -> int:
+    if pos_offset is None:
+        pos_offset = n_k - n_q
+    a = attn_args(B, n_q, n_k, pos_offset, H, D, topk, 0.0)
+    n = ctypes.c_size_t(0)
+    _check(L.load().dsa_attn_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return given
+    if given is not None:
+        if given.numel() * given.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return given
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class IndexerResult:
+    idx: torch.Tensor                    # [B, n_q, topk] int32
+    scores: Optional[torch.Tensor]       # [B, n_q, topk] fp32
+    full_scores: Optional[torch.Tensor]  # [B, n_q, n_k] fp32 (test mode)
+
+
+def indexer_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk: int, *,
+                        q_scale: Optional[torch.Tensor] = None,
+                        k_scale: Optional[torch.Tensor] = None,
+                        pos_offset: Optional[int] = None,
+                        out_idx: Optional[torch.Tensor] = None,
+                        out_scores=False, debug_full_scores=False,
+                        workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> IndexerResult:
+    """Lightning-indexer scores + exact per-query top-k (dsa_indexer_scores_topk).
+
+    q [B, n_q, H, D], k [B, n_k, D] (bf16 or float8_e4m3fn), w [B, n_q, H] fp32,
+    fp8: q_scale [B, n_q], k_scale [B, n_k] fp32. out_scores / debug_full_scores
+    may be True (allocate), a tensor, or False. debug_full_scores is pre-filled
+    with NaN so that the entries the kernel does not write stay recognisable."""
+    _need(q, "q", ndim=4)
+    B, n_q, H, D = q.shape
+    _need(k, "k", dtype=q.dtype, ndim=3)
+    n_k = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != D:
+        raise ValueError("k must be [B, n_k, D]")
+    _need(w, "w", dtype=torch.float32, ndim=3)
+    if tuple(w.shape) != (B, n_q, H):
+        raise ValueError("w must be [B, n_q, H]")
+    code = _dtype_code(q)
+    if code == L.DSA_FP8_E4M3FN:
+        _need(q_scale, "q_scale", dtype=torch.float32, ndim=2)
+        _need(k_scale, "k_scale", dtype=torch.float32, ndim=2)
+        if tuple(q_scale.shape) != (B, n_q) or tuple(k_scale.shape) != (B, n_k):
+            raise ValueError("q_scale must be [B, n_q] and k_scale [B, n_k]")
+    if pos_offset is None:
+        pos_offset = n_k - n_q
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((B, n_q, topk), dtype=torch.int32, device=dev)
+    else:
+        _need(out_idx, "out_idx", dtype=torch.int32)
+        if tuple(out_idx.shape) != (B, n_q, topk):
+            raise ValueError("out_idx must be [B, n_q, topk]")
+    sc = None
+    if out_scores is True:
+        sc = torch.empty((B, n_q, topk), dtype=torch.float32, device=dev)
+    elif isinstance(out_scores, torch.Tensor):
+        sc = out_scores
+    full = None
+    if debug_full_scores is True:
+        full = torch.full((B, n_q, n_k), float("nan"), dtype=torch.float32, device=dev)
+    elif isinstance(debug_full_scores, torch.Tensor):
+        full = debug_full_scores
+    a = indexer_args(B, n_q, n_k, pos_offset, H, D, topk, code)
+    nbytes = ctypes.c_size_t(0)
+    _check(L.load().dsa_indexer_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws = _workspace(int(nbytes.value), dev, workspace)
+    a.q, a.k, a.w = _ptr(q), _ptr(k), _ptr(w)
+    a.q_scale, a.k_scale = _ptr(q_scale), _ptr(k_scale)
+    a.out_idx, a.out_scores, a.debug_full_scores = _ptr(out_idx), _ptr(sc), _ptr(full)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(L.load().dsa_indexer_scores_topk(ctypes.byref(a), _stream(stream)))
+    return IndexerResult(out_idx, sc, full)
+
+
+def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, *,
+                scale: float = 0.0, pos_offset: Optional[int] = None,
+                out: Optional[torch.Tensor] = None, lse=False,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """Sparse attention (dsa_sparse_attn): q [B, n_q, H, D], k/v [B, n_k, D] bf16,
+    idx [B, n_q, topk] int32. Returns (out bf16 [B, n_q, H, D], lse or None)."""
+    _need(q, "q", dtype=torch.bfloat16, ndim=4)
+    B, n_q, H, D = q.shape
+    _need(k, "k", dtype=torch.bfloat16, ndim=3)
+    _need(v, "v", dtype=torch.bfloat16, ndim=3)
+    n_k = k.shape[1]
+    if tuple(k.shape) != (B, n_k, D) or tuple(v.shape) != (B, n_k, D):
+        raise ValueError("k and v must be [B, n_k, D]")
+    _need(idx, "idx", dtype=torch.int32, ndim=3)
+    if idx.shape[0] != B or idx.shape[1] != n_q:
+        raise ValueError("idx must be [B, n_q, topk]")
+    topk = idx.shape[2]
+    if pos_offset is None:
+        pos_offset = n_k - n_q
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, n_q, H, D), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", dtype=torch.bfloat16)
+    lse_t = None
+    if lse is True:
+        lse_t = torch.empty((B, n_q, H), dtype=torch.float32, device=dev)
+    elif isinstance(lse, torch.Tensor):
+        lse_t = lse
+    a = attn_args(B, n_q, n_k, pos_offset, H, D, topk, scale)
+    nbytes = ctypes.c_size_t(0)
+    _check(L.load().dsa_attn_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws = _workspace(int(nbytes.value), dev, workspace)
+    a.q, a.k, a.v, a.idx, a.out, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out), _ptr(lse_t)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(L.load().dsa_sparse_attn(ctypes.byref(a), _stream(stream)))
+    return out, lse_t
+
+
+def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+class LayerStack:
+    """A prepared dsa_layer_stack_run call: per-layer tensors, the shared index
+    buffer (IndexCache's cache) and one workspace, reusable across runs."""
+
+    def __init__(self, layers: List[dict], topk: int, *, scale: float = 0.0,
+                 pos_offset: Optional[int] = None, lse: bool = False, shared_out: bool = False,
+                 events: bool = False):
+        l0 = layers[0]
+        B, n_q, H_I, D_I = l0["q_idx"].shape
+        n_k = l0["k_idx"].shape[1]
+        _, _, H, D = l0["q"].shape
+        if pos_offset is None:
+            pos_offset = n_k - n_q
+        code = _dtype_code(l0["q_idx"])
+        fp8 = code == L.DSA_FP8_E4M3FN
+        dev = l0["q"].device
+        for i, ly in enumerate(layers):
+            _need(ly["q_idx"], f"layers[{i}].q_idx", dtype=l0["q_idx"].dtype)
+            _need(ly["k_idx"], f"layers[{i}].k_idx", dtype=l0["q_idx"].dtype)
+            _need(ly["w"], f"layers[{i}].w", dtype=torch.float32)
+            for nm in ("q", "k", "v"):
+                _need(ly[nm], f"layers[{i}].{nm}", dtype=torch.bfloat16)
+            if tuple(ly["q_idx"].shape) != (B, n_q, H_I, D_I) or tuple(ly["q"].shape) != (B, n_q, H, D):
+                raise ValueError(f"layer {i}: shapes differ from layer 0")
+        self.layers = layers
+        self.idx_buf = torch.empty((B, n_q, topk), dtype=torch.int32, device=dev)
+        if shared_out:
+            o = torch.empty((B, n_q, H, D), dtype=torch.bfloat16, device=dev)
+            self.outs = [o] * len(layers)
+        else:
+            self.outs = [torch.empty((B, n_q, H, D), dtype=torch.bfloat16, device=dev) for _ in layers]
+        self.lses = ([torch.empty((B, n_q, H), dtype=torch.float32, device=dev) for _ in layers]
+                     if lse else None)
+        a = L.StackArgs()
+        a.struct_size = ctypes.sizeof(L.StackArgs)
+        a.n_layers = len(layers)
+        a.indexer = indexer_args(B, n_q, n_k, pos_offset, H_I, D_I, topk, code)
+        a.attn = attn_args(B, n_q, n_k, pos_offset, H, D, topk, scale)
+        self._keep = [
+            _ptr_array([ly["q_idx"] for ly in layers]), _ptr_array([ly["k_idx"] for ly in layers]),
+            _ptr_array([ly["w"] for ly in layers]),
+            _ptr_array([ly["q_scale"] for ly in layers]) if fp8 else None,
+            _ptr_array([ly["k_scale"] for ly in layers]) if fp8 else None,
+            _ptr_array([ly["q"] for ly in layers]), _ptr_array([ly["k"] for ly in layers]),
+            _ptr_array([ly["v"] for ly in layers]), _ptr_array(self.outs),
+            _ptr_array(self.lses) if self.lses is not None else None,
+        ]
+        names = ["q_idx", "k_idx", "w", "q_scale", "k_scale", "q", "k", "v", "out", "lse"]
+        for nm, arr in zip(names, self._keep):
+            setattr(a, nm, None if arr is None else ctypes.cast(arr, ctypes.c_void_p))
+        a.idx_buf = _ptr(self.idx_buf)
+        self.events = None
+        if events:
+            self.events = [torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)]
+            # torch.cuda.Event creates its hipEvent lazily; record once to materialise it.
+            for e in self.events:
+                e.record()
+            ev = (ctypes.c_void_p * len(self.events))()
+            for i, e in enumerate(self.events):
+                ev[i] = e.cuda_event
+            self._keep.append(ev)
+            a.layer_events = ctypes.cast(ev, ctypes.c_void_p)
+        n = ctypes.c_size_t(0)
+        _check(L.load().dsa_stack_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+        self.workspace = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+        a.workspace = _ptr(self.workspace)
+        a.workspace_bytes = self.workspace.numel()
+        self.args = a
+
+    def run(self, pattern: Optional[str] = None, freq: int = 0, stream=None):
+        pat = None if pattern is None else pattern.encode()
+        _check(L.load().dsa_layer_stack_run(ctypes.byref(self.args), pat, int(freq), _stream(stream)))
+        return self.idx_buf, self.outs, self.lses
+
+    def layer_times_ms(self) -> List[float]:
+        """Per-layer durations from the recorded layer events (after a sync)."""
+        if not self.events:
+            raise RuntimeError("created without events=True")
+        return [self.events[i].elapsed_time(self.events[i + 1]) for i in range(len(self.events) - 1)]

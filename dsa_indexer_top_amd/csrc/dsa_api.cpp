@@ -1,0 +1,415 @@
+// Host side of libdsa: argument validation, IndexCache pattern resolution,
+// workspace sizing and kernel dispatch. Every check runs before the first HIP
+// call, so an invalid call touches no output and needs no GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool count4(int64_t a, int64_t b, int64_t c, int64_t d, int64_t* out) {
+  int64_t x, y;
+  return mul_ok(a, b, &x) && mul_ok(x, c, &y) && mul_ok(y, d, out);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxAttnTopk = 4096;
+constexpr int kMaxB = 65535;
+
+dsa_status check_indexer_shape(const dsa_indexer_args* a, const char* what) {
+  if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: args is NULL", what);
+  if (a->struct_size != sizeof(dsa_indexer_args))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: struct_size %u != %zu", what, a->struct_size,
+                sizeof(dsa_indexer_args));
+  if (a->B < 1 || a->B > kMaxB) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: B=%d out of 1..%d", what, a->B, kMaxB);
+  if (a->n_q < 1 || a->n_k < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: n_q=%d n_k=%d must be >= 1", what, a->n_q, a->n_k);
+  if (a->q_pos_offset < 0 || (int64_t)a->q_pos_offset + a->n_q > a->n_k)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: need 0 <= q_pos_offset and q_pos_offset + n_q <= n_k (%d + %d vs %d)",
+                what, a->q_pos_offset, a->n_q, a->n_k);
+  if (a->dtype != DSA_BF16 && a->dtype != DSA_FP8_E4M3FN)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: dtype %d unsupported", what, a->dtype);
+  if (a->n_heads < 1 || a->n_heads > 64)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: n_heads=%d outside 1..64", what, a->n_heads);
+  const int d = a->head_dim;
+  const bool d_ok = a->dtype == DSA_BF16 ? (d == 32 || d == 64 || d == 128) : (d == 64 || d == 128);
+  if (!d_ok) return fail(DSA_ERR_UNSUPPORTED, "%s: head_dim=%d unsupported for this dtype", what, d);
+  if (a->topk < 1 || a->topk > kMaxTopk)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: topk=%d outside 1..%d", what, a->topk, kMaxTopk);
+  int64_t n;
+  if (!count4(a->B, a->n_q, a->n_heads, a->head_dim, &n) || !count4(a->B, a->n_q, a->n_k, 1, &n) ||
+      !count4(a->B, a->n_q, dsa::cand_capacity(a->topk), 8, &n))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: sizes overflow int64", what);
+  return DSA_OK;
+}
+
+dsa_status check_attn_shape(const dsa_attn_args* a, const char* what) {
+  if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: args is NULL", what);
+  if (a->struct_size != sizeof(dsa_attn_args))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: struct_size %u != %zu", what, a->struct_size,
+                sizeof(dsa_attn_args));
+  if (a->B < 1 || a->B > kMaxB) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: B=%d out of 1..%d", what, a->B, kMaxB);
+  if (a->n_q < 1 || a->n_k < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: n_q=%d n_k=%d must be >= 1", what, a->n_q, a->n_k);
+  if (a->q_pos_offset < 0 || (int64_t)a->q_pos_offset + a->n_q > a->n_k)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: need 0 <= q_pos_offset and q_pos_offset + n_q <= n_k", what);
+  if (a->n_heads < 1 || a->n_heads > 16)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: n_heads=%d outside 1..16", what, a->n_heads);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: head_dim=%d unsupported (64, 128)", what, a->head_dim);
+  if (a->topk < 1 || a->topk > kMaxAttnTopk)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: topk=%d outside 1..%d", what, a->topk, kMaxAttnTopk);
+  if (!(a->scale >= 0.0f) || a->scale > 3.0e38f)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: scale must be finite and >= 0", what);
+  int64_t n;
+  if (!count4(a->B, a->n_q, a->n_heads, a->head_dim, &n) || !count4(a->B, a->n_q, a->topk, 1, &n) ||
+      !count4(a->B, a->n_k, a->head_dim, 1, &n))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: sizes overflow int64", what);
+  return DSA_OK;
+}
+
+dsa_status check_indexer_ptrs(const dsa_indexer_args* a, const void* q, const void* k, const float* w,
+                              const float* qs, const float* ks, const int32_t* out_idx, const char* what) {
+  if (!q || !k || !w || !out_idx) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: q, k, w and out_idx are required", what);
+  if (a->dtype == DSA_FP8_E4M3FN && (!qs || !ks))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: fp8 needs q_scale and k_scale", what);
+  if (a->dtype == DSA_BF16 && (qs || ks))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: q_scale/k_scale must be NULL for bf16", what);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(out_idx, 4) ||
+      (qs && !aligned(qs, 4)) || (ks && !aligned(ks, 4)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: misaligned pointer (q, k: 16 bytes; others: 4)", what);
+  return DSA_OK;
+}
+
+dsa_status check_attn_ptrs(const void* q, const void* k, const void* v, const int32_t* idx, const void* out,
+                           const float* lse, const char* what) {
+  if (!q || !k || !v || !idx || !out) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: q, k, v, idx and out are required", what);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) || !aligned(out, 4) ||
+      (lse && !aligned(lse, 4)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: misaligned pointer (q, k, v: 16 bytes; others: 4)", what);
+  return DSA_OK;
+}
+
+dsa_status check_workspace(void* ws, size_t have, size_t need, const char* what) {
+  if (need == 0) return DSA_OK;
+  if (!ws) return fail(DSA_ERR_WORKSPACE, "%s: workspace is NULL but %zu bytes are needed", what, need);
+  if (have < need) return fail(DSA_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", what, have, need);
+  if (!aligned(ws, 256)) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", what);
+  return DSA_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+dsa::IndexerParams make_indexer_params(const dsa_indexer_args* a, const void* q, const void* k, const float* w,
+                                       const float* qs, const float* ks, int32_t* out_idx, float* out_scores,
+                                       float* dump, void* ws) {
+  dsa::IndexerParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = a->B;
+  p.n_q = a->n_q;
+  p.n_k = a->n_k;
+  p.pos_offset = a->q_pos_offset;
+  p.H = a->n_heads;
+  p.D = a->head_dim;
+  p.topk = a->topk;
+  p.fp8 = a->dtype == DSA_FP8_E4M3FN;
+  p.q = q;
+  p.k = k;
+  p.w = w;
+  p.q_scale = qs;
+  p.k_scale = ks;
+  p.out_idx = out_idx;
+  p.out_scores = out_scores;
+  p.dump = dump;
+  dsa::indexer_bind_workspace(p, ws);
+  return p;
+}
+
+dsa::AttnParams make_attn_params(const dsa_attn_args* a, const void* q, const void* k, const void* v,
+                                 const int32_t* idx, void* out, float* lse, void* ws) {
+  dsa::AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.B = a->B;
+  p.n_q = a->n_q;
+  p.n_k = a->n_k;
+  p.pos_offset = a->q_pos_offset;
+  p.H = a->n_heads;
+  p.D = a->head_dim;
+  p.topk = a->topk;
+  p.scale = a->scale > 0.0f ? a->scale : 1.0f / sqrtf((float)a->head_dim);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.idx = idx;
+  p.out = out;
+  p.lse = lse;
+  p.nsplit = dsa::attn_nsplit(a->B, a->n_q, a->topk);
+  p.part = (float*)ws;
+  return p;
+}
+
+dsa_status run_indexer(const dsa::IndexerParams& p, hipStream_t s) {
+  const hipError_t e = p.n_q == 1 ? dsa::launch_indexer_decode(p, s) : dsa::launch_indexer_prefill(p, s);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "indexer launch failed: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
+dsa_status run_attn(const dsa::AttnParams& p, hipStream_t s) {
+  const hipError_t e = dsa::launch_sparse_attn(p, s);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "sparse attention launch failed: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
+}  // namespace
+
+namespace dsa {
+
+size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk) {
+  const size_t rows = (size_t)B * n_q;
+  const size_t C = (size_t)cand_capacity(topk);
+  size_t sz = 0;
+  sz += round_up(rows * C * 4, 256);  // cand_key
+  sz += round_up(rows * C * 4, 256);  // cand_idx
+  sz += round_up(rows * 4, 256);      // cand_cnt
+  if (n_q == 1) {
+    sz += round_up((size_t)B * n_k * 4, 256);                // decode keys
+    sz += round_up((size_t)B * kDecodeHistBins * 4, 256);    // decode histogram
+  }
+  return sz;
+}
+
+void indexer_bind_workspace(IndexerParams& p, void* ws) {
+  const size_t rows = (size_t)p.B * p.n_q;
+  p.C = cand_capacity(p.topk);
+  char* c = (char*)ws;
+  p.cand_key = (uint32_t*)c;
+  c += round_up(rows * p.C * 4, 256);
+  p.cand_idx = (int32_t*)c;
+  c += round_up(rows * p.C * 4, 256);
+  p.cand_cnt = (int32_t*)c;
+  c += round_up(rows * 4, 256);
+  if (p.n_q == 1) {
+    p.dec_keys = (uint32_t*)c;
+    c += round_up((size_t)p.B * p.n_k * 4, 256);
+    p.dec_hist = (uint32_t*)c;
+  }
+}
+
+int attn_nsplit(int B, int n_q, int topk) {
+  if (n_q > 1) return 1;
+  // decode: spread one request's gather over many waves (>= 64 entries each)
+  int ns = topk / 64;
+  if (ns < 1) ns = 1;
+  if (ns > 64) ns = 64;
+  (void)B;
+  return ns;
+}
+
+size_t attn_workspace_bytes(int B, int n_q, int n_k, int H, int D, int topk) {
+  (void)n_k;
+  const int ns = attn_nsplit(B, n_q, topk);
+  if (ns <= 1) return 0;
+  return round_up((size_t)B * n_q * ns * H * (D + 2) * 4, 256);
+}
+
+}  // namespace dsa
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(dsa_status st) {
+  switch (st) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARGUMENT: return "DSA_ERR_INVALID_ARGUMENT";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_BAD_PATTERN: return "DSA_ERR_BAD_PATTERN";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+dsa_status dsa_resolve_pattern(int32_t n_layers, const char* pattern, int32_t freq, char* out) {
+  if (!out) return fail(DSA_ERR_INVALID_ARGUMENT, "resolve_pattern: out is NULL");
+  if (n_layers < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "resolve_pattern: n_layers=%d must be >= 1", n_layers);
+  if (freq < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "resolve_pattern: index_topk_freq=%d must be >= 0", freq);
+  if (pattern && freq > 0)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "resolve_pattern: index_topk_pattern and index_topk_freq are alternatives");
+  if (pattern) {
+    const size_t len = strnlen(pattern, (size_t)n_layers + 1);
+    if (len != (size_t)n_layers)
+      return fail(DSA_ERR_BAD_PATTERN, "resolve_pattern: pattern length %zu%s != n_layers %d", len,
+                  len > (size_t)n_layers ? "+" : "", n_layers);
+    for (int l = 0; l < n_layers; ++l)
+      if (pattern[l] != 'F' && pattern[l] != 'S')
+        return fail(DSA_ERR_BAD_PATTERN, "resolve_pattern: character %d is '%c', not 'F' or 'S'", l, pattern[l]);
+    if (pattern[0] != 'F') return fail(DSA_ERR_BAD_PATTERN, "resolve_pattern: the first layer must be 'F'");
+    memcpy(out, pattern, (size_t)n_layers);
+  } else {
+    for (int l = 0; l < n_layers; ++l) out[l] = (freq > 0 && l % freq != 0) ? 'S' : 'F';
+  }
+  out[n_layers] = '\0';
+  return ok();
+}
+
+dsa_status dsa_indexer_workspace_size(const dsa_indexer_args* a, size_t* bytes) {
+  dsa_status st = check_indexer_shape(a, "indexer_workspace_size");
+  if (st != DSA_OK) return st;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARGUMENT, "indexer_workspace_size: bytes is NULL");
+  *bytes = dsa::indexer_workspace_bytes(a->B, a->n_q, a->n_k, a->topk);
+  return ok();
+}
+
+dsa_status dsa_attn_workspace_size(const dsa_attn_args* a, size_t* bytes) {
+  dsa_status st = check_attn_shape(a, "attn_workspace_size");
+  if (st != DSA_OK) return st;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARGUMENT, "attn_workspace_size: bytes is NULL");
+  *bytes = dsa::attn_workspace_bytes(a->B, a->n_q, a->n_k, a->n_heads, a->head_dim, a->topk);
+  return ok();
+}
+
+static dsa_status check_stack_shape(const dsa_stack_args* a, const char* what) {
+  if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: args is NULL", what);
+  if (a->struct_size != sizeof(dsa_stack_args))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: struct_size %u != %zu", what, a->struct_size, sizeof(dsa_stack_args));
+  if (a->n_layers < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: n_layers=%d must be >= 1", what, a->n_layers);
+  dsa_status st = check_indexer_shape(&a->indexer, what);
+  if (st != DSA_OK) return st;
+  st = check_attn_shape(&a->attn, what);
+  if (st != DSA_OK) return st;
+  const dsa_indexer_args& i = a->indexer;
+  const dsa_attn_args& t = a->attn;
+  if (i.B != t.B || i.n_q != t.n_q || i.n_k != t.n_k || i.q_pos_offset != t.q_pos_offset || i.topk != t.topk)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: indexer and attention shapes disagree (B, n_q, n_k, offset, topk)", what);
+  return DSA_OK;
+}
+
+static size_t stack_ws(const dsa_stack_args* a) {
+  const size_t wi = dsa::indexer_workspace_bytes(a->indexer.B, a->indexer.n_q, a->indexer.n_k, a->indexer.topk);
+  const size_t wa = dsa::attn_workspace_bytes(a->attn.B, a->attn.n_q, a->attn.n_k, a->attn.n_heads,
+                                              a->attn.head_dim, a->attn.topk);
+  return wi > wa ? wi : wa;
+}
+
+dsa_status dsa_stack_workspace_size(const dsa_stack_args* a, size_t* bytes) {
+  dsa_status st = check_stack_shape(a, "stack_workspace_size");
+  if (st != DSA_OK) return st;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARGUMENT, "stack_workspace_size: bytes is NULL");
+  *bytes = stack_ws(a);
+  return ok();
+}
+
+dsa_status dsa_indexer_scores_topk(const dsa_indexer_args* a, void* stream) {
+  const char* what = "indexer_scores_topk";
+  dsa_status st = check_indexer_shape(a, what);
+  if (st != DSA_OK) return st;
+  st = check_indexer_ptrs(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx, what);
+  if (st != DSA_OK) return st;
+  if ((a->out_scores && !aligned(a->out_scores, 4)) || (a->debug_full_scores && !aligned(a->debug_full_scores, 4)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: misaligned out_scores/debug_full_scores", what);
+  const size_t need = dsa::indexer_workspace_bytes(a->B, a->n_q, a->n_k, a->topk);
+  st = check_workspace(a->workspace, a->workspace_bytes, need, what);
+  if (st != DSA_OK) return st;
+  const dsa::IndexerParams p = make_indexer_params(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx,
+                                                   a->out_scores, a->debug_full_scores, a->workspace);
+  st = run_indexer(p, (hipStream_t)stream);
+  return st == DSA_OK ? ok() : st;
+}
+
+dsa_status dsa_sparse_attn(const dsa_attn_args* a, void* stream) {
+  const char* what = "sparse_attn";
+  dsa_status st = check_attn_shape(a, what);
+  if (st != DSA_OK) return st;
+  st = check_attn_ptrs(a->q, a->k, a->v, a->idx, a->out, a->lse, what);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa::attn_workspace_bytes(a->B, a->n_q, a->n_k, a->n_heads, a->head_dim, a->topk);
+  st = check_workspace(a->workspace, a->workspace_bytes, need, what);
+  if (st != DSA_OK) return st;
+  const dsa::AttnParams p = make_attn_params(a, a->q, a->k, a->v, a->idx, a->out, a->lse, a->workspace);
+  st = run_attn(p, (hipStream_t)stream);
+  return st == DSA_OK ? ok() : st;
+}
+
+dsa_status dsa_layer_stack_run(const dsa_stack_args* a, const char* pattern, int32_t freq, void* stream) {
+  const char* what = "layer_stack_run";
+  dsa_status st = check_stack_shape(a, what);
+  if (st != DSA_OK) return st;
+  const int n = a->n_layers;
+  std::string P((size_t)n + 1, '\0');
+  st = dsa_resolve_pattern(n, pattern, freq, &P[0]);
+  if (st != DSA_OK) return st;
+  if (!a->q_idx || !a->k_idx || !a->w || !a->q || !a->k || !a->v || !a->out || !a->idx_buf)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: per-layer arrays and idx_buf are required", what);
+  const bool fp8 = a->indexer.dtype == DSA_FP8_E4M3FN;
+  if (fp8 && (!a->q_scale || !a->k_scale))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: fp8 needs q_scale and k_scale arrays", what);
+  if (!fp8 && (a->q_scale || a->k_scale))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: q_scale/k_scale arrays must be NULL for bf16", what);
+  if (!aligned(a->idx_buf, 4)) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: misaligned idx_buf", what);
+  for (int l = 0; l < n; ++l) {
+    // S layers never read their indexer inputs, but the arrays are validated for
+    // every layer so that the same arguments run under any pattern.
+    st = check_indexer_ptrs(&a->indexer, a->q_idx[l], a->k_idx[l], a->w[l], fp8 ? a->q_scale[l] : nullptr,
+                            fp8 ? a->k_scale[l] : nullptr, a->idx_buf, what);
+    if (st != DSA_OK) return fail(st, "%s (layer %d)", dsa_last_error(), l);
+    st = check_attn_ptrs(a->q[l], a->k[l], a->v[l], a->idx_buf, a->out[l], a->lse ? a->lse[l] : nullptr, what);
+    if (st != DSA_OK) return fail(st, "%s (layer %d)", dsa_last_error(), l);
+  }
+  st = check_workspace(a->workspace, a->workspace_bytes, stack_ws(a), what);
+  if (st != DSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  for (int l = 0; l < n; ++l) {
+    if (a->layer_events) {
+      const hipError_t e = hipEventRecord((hipEvent_t)a->layer_events[l], s);
+      if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipEventRecord: %s", what, hipGetErrorString(e));
+    }
+    if (P[(size_t)l] == 'F') {
+      // F layer: compute fresh indices and overwrite the single cached buffer
+      const dsa::IndexerParams ip = make_indexer_params(&a->indexer, a->q_idx[l], a->k_idx[l], a->w[l],
+                                                        fp8 ? a->q_scale[l] : nullptr, fp8 ? a->k_scale[l] : nullptr,
+                                                        a->idx_buf, nullptr, nullptr, a->workspace);
+      st = run_indexer(ip, s);
+      if (st != DSA_OK) return st;
+    }
+    // every layer: sparse attention over the cached indices
+    const dsa::AttnParams ap = make_attn_params(&a->attn, a->q[l], a->k[l], a->v[l], a->idx_buf, a->out[l],
+                                                a->lse ? a->lse[l] : nullptr, a->workspace);
+    st = run_attn(ap, s);
+    if (st != DSA_OK) return st;
+  }
+  if (a->layer_events) {
+    const hipError_t e = hipEventRecord((hipEvent_t)a->layer_events[n], s);
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipEventRecord: %s", what, hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal interface between the host API (dsa_api.cpp) and the kernel
+// launchers (*.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Candidate-list capacity per query row of the streaming top-k: room for the
+// k kept winners plus at least two 64-key tiles of new arrivals.
+inline int cand_capacity(int topk) {
+  int c = topk * 2;
+  if (c < topk + 128) c = topk + 128;
+  return (c + 63) / 64 * 64;
+}
+
+// Decode path: bins of the first-level histogram of the 32-bit score keys.
+constexpr int kDecodeHistBits = 12;
+constexpr int kDecodeHistBins = 1 << kDecodeHistBits;
+constexpr int kDecodeKeysPerBlock = 256;
+constexpr int kDecodeCollectBlocks = 64;
+
+struct IndexerParams {
+  int B, n_q, n_k, pos_offset, H, D, topk, fp8;
+  const void* q;
+  const void* k;
+  const float* w;
+  const float* q_scale;
+  const float* k_scale;
+  int32_t* out_idx;
+  float* out_scores;
+  float* dump;
+  // workspace views
+  uint32_t* cand_key;   // [rows, C]
+  int32_t* cand_idx;    // [rows, C]
+  int32_t* cand_cnt;    // [rows]
+  int C;
+  uint32_t* dec_keys;   // decode: [B, n_k] score keys
+  uint32_t* dec_hist;   // decode: [B, kDecodeHistBins]
+};
+
+struct AttnParams {
+  int B, n_q, n_k, pos_offset, H, D, topk;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  void* out;
+  float* lse;
+  int nsplit;           // >1: split-K over the idx list (decode), partials in ws
+  float* part;          // [rows, nsplit, H, D + 2]
+};
+
+size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk);
+size_t attn_workspace_bytes(int B, int n_q, int n_k, int H, int D, int topk);
+int attn_nsplit(int B, int n_q, int topk);
+
+// Carves the workspace into the views above.
+void indexer_bind_workspace(IndexerParams& p, void* ws);
+
+hipError_t launch_indexer_prefill(const IndexerParams& p, hipStream_t s);
+hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s);
+hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,217 @@
+/*
+ * dsa.h - C ABI of libdsa: the DeepSeek-Sparse-Attention hot path on AMD
+ * Instinct MI355X (gfx950): the lightning indexer fused with per-query top-k
+ * selection, sparse attention over the selected tokens, and the IndexCache
+ * layer stack in which Full (F) layers compute the indices and Shared (S)
+ * layers reuse them.
+ *
+ * Sources.
+ *  - "IndexCache: Accelerating Sparse Attention via Cross-Layer Index Reuse"
+ *    (arXiv 2603.12201), Abstract: a lightweight lightning indexer picks the
+ *    top-k tokens for each query and core attention runs over those tokens
+ *    only (O(L*k) instead of O(L^2)); the indexer itself stays O(L^2) and runs
+ *    at every layer; IndexCache lets Shared layers reuse the indices of a Full
+ *    layer.
+ *  - Same paper, Figure 2 caption: one conditional branch in the layer loop;
+ *    the cached index tensor is a temporary buffer holding only the current
+ *    indices, overwritten at each F layer, needing no memory beyond plain DSA.
+ *  - IndexCache repository README, "Step 3: Launch with IndexCache": the two
+ *    configuration keys index_topk_freq (Option A, uniform interleaving) and
+ *    index_topk_pattern (Option B, one 'F'/'S' character per DSA layer), and
+ *    "Default behavior" (neither key: every layer runs its indexer).
+ * The pages name the indexer but do not print its formula; this library
+ * computes the standard DSA indexer score
+ *      I[t,s] = sum_j w[t,j] * ReLU( q[t,j,:] . k[s,:] ),  0 <= s <= pos(t),
+ * where pos(t) = q_pos_offset + t. For fp8 inputs the dequantised operands are
+ * e4m3(q)*q_scale[t] and e4m3(k)*k_scale[s].
+ *
+ * Conventions (every function):
+ *  - Ownership: the caller owns every device buffer and the stream. The
+ *    library allocates no device memory and keeps no device state; scratch
+ *    space is the caller's workspace, sized by the *_workspace_size calls.
+ *  - Layouts: every tensor is dense row-major with the last dimension
+ *    contiguous, exactly in the shapes documented below (no strides).
+ *  - Pointers are device pointers unless stated; they must be aligned to
+ *    16 bytes (workspace: 256 bytes).
+ *  - Execution: asynchronous on `stream` (a hipStream_t passed as void*,
+ *    NULL = the null stream); nothing synchronises inside the library.
+ *  - Validation happens on the host before the first HIP call: on any error
+ *    the call returns a status, sets dsa_last_error() (thread-local text) and
+ *    touches no output.
+ *  - Index outputs are int32, in rank order (higher score first, equal
+ *    scores by lower index first; -0.0 equals +0.0), padded with -1 when a
+ *    query has fewer than topk causal keys.
+ *  - Sizes are validated in 64-bit arithmetic; every element count must fit
+ *    in int64 and every per-dimension size in int32.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, bad size, misaligned pointer */
+  DSA_ERR_UNSUPPORTED = 2,      /* shape or dtype outside the supported set   */
+  DSA_ERR_BAD_PATTERN = 3,      /* index_topk_pattern string rejected         */
+  DSA_ERR_WORKSPACE = 4,        /* workspace missing or too small             */
+  DSA_ERR_HIP = 5               /* a HIP runtime call or launch failed        */
+} dsa_status;
+
+typedef enum {
+  DSA_BF16 = 0,        /* bfloat16 q_idx / k_idx                               */
+  DSA_FP8_E4M3FN = 1   /* OCP fp8 e4m3fn q_idx / k_idx + fp32 per-token scales */
+} dsa_dtype;
+
+/* Indexer + top-k for B independent sequences (prefill) or requests (decode).
+ *
+ *   q        [B, n_q, n_heads, head_dim]  bf16 or e4m3fn (query-side indexer
+ *                                          vectors, one per indexer head)
+ *   k        [B, n_k, head_dim]           same dtype (indexer keys)
+ *   w        [B, n_q, n_heads]            fp32 per-query head weights
+ *   q_scale  [B, n_q] fp32, k_scale [B, n_k] fp32: fp8 only (> 0), NULL for bf16
+ *   out_idx  [B, n_q, topk] int32          selected key indices, rank order
+ *   out_scores [B, n_q, topk] fp32         optional (NULL): score of each
+ *                                          selected key (-inf where idx = -1)
+ *   debug_full_scores [B, n_q, n_k] fp32   optional (NULL), test mode: the
+ *                                          same kernel also stores every causal
+ *                                          score it computes (non-causal
+ *                                          entries are left untouched)
+ * Query t of a sequence sits at position q_pos_offset + t and sees keys
+ * 0..min(q_pos_offset + t, n_k - 1). Requires 0 <= q_pos_offset and
+ * q_pos_offset + n_q <= n_k. n_q == 1 selects the decode path (the one query's
+ * keys are spread over the whole GPU); n_q > 1 the prefill path.
+ * Supported: n_heads in 1..64, head_dim in {32, 64, 128} (fp8: {64, 128}),
+ * topk in 1..2048. */
+typedef struct {
+  uint32_t struct_size;         /* = sizeof(dsa_indexer_args) */
+  int32_t B, n_q, n_k, q_pos_offset;
+  int32_t n_heads, head_dim, topk;
+  int32_t dtype;                /* dsa_dtype */
+  const void *q;
+  const void *k;
+  const float *w;
+  const float *q_scale;
+  const float *k_scale;
+  int32_t *out_idx;
+  float *out_scores;
+  float *debug_full_scores;
+  void *workspace;
+  size_t workspace_bytes;
+} dsa_indexer_args;
+
+/* Sparse attention over given indices, one KV head shared by n_heads query
+ * heads (bf16 in, fp32 softmax, bf16 out).
+ *
+ *   q    [B, n_q, n_heads, head_dim] bf16;  k, v [B, n_k, head_dim] bf16
+ *   idx  [B, n_q, topk] int32: entries < 0, > q_pos_offset + t or >= n_k are
+ *        skipped (so -1 padding is ignored); duplicates count once each
+ *   out  [B, n_q, n_heads, head_dim] bf16 (softmax-normalised)
+ *   lse  [B, n_q, n_heads] fp32, optional (NULL): natural-log sum-exp of the
+ *        scaled scores (-inf and out = 0 for a query with no valid entry)
+ * scale = 0 means 1/sqrt(head_dim). Supported: n_heads in 1..16, head_dim in
+ * {64, 128}, topk in 1..4096. */
+typedef struct {
+  uint32_t struct_size;         /* = sizeof(dsa_attn_args) */
+  int32_t B, n_q, n_k, q_pos_offset;
+  int32_t n_heads, head_dim, topk;
+  float scale;
+  const void *q;
+  const void *k;
+  const void *v;
+  const int32_t *idx;
+  void *out;
+  float *lse;
+  void *workspace;
+  size_t workspace_bytes;
+} dsa_attn_args;
+
+/* A stack of n_layers DSA layers, each = (indexer + top-k if F) + sparse
+ * attention, with one shared index buffer (the IndexCache cache).
+ *
+ * `indexer` and `attn` give the shapes and dtype shared by all layers; their
+ * pointer fields (and workspace fields) are ignored. The per-layer pointers
+ * are HOST arrays of n_layers DEVICE pointers. q_scale / k_scale arrays are
+ * required for fp8 and must be NULL for bf16. lse may be NULL (no lse) or an
+ * array whose entries may be NULL. out entries may alias each other.
+ * idx_buf [B, n_q, topk] int32 is the single cached index tensor: every F
+ * layer overwrites it, every S layer reads it; after the call it holds the
+ * indices of the last F layer. layer_events, if not NULL, is a host array of
+ * n_layers + 1 hipEvent_t (as void*): event l is recorded before layer l and
+ * event n_layers after the last layer. The workspace size does not depend on
+ * the pattern. */
+typedef struct {
+  uint32_t struct_size;         /* = sizeof(dsa_stack_args) */
+  int32_t n_layers;
+  dsa_indexer_args indexer;
+  dsa_attn_args attn;
+  const void *const *q_idx;
+  const void *const *k_idx;
+  const float *const *w;
+  const float *const *q_scale;
+  const float *const *k_scale;
+  const void *const *q;
+  const void *const *k;
+  const void *const *v;
+  void *const *out;
+  float *const *lse;
+  int32_t *idx_buf;
+  void *const *layer_events;
+  void *workspace;
+  size_t workspace_bytes;
+} dsa_stack_args;
+
+/* DSA_ABI_VERSION of the built library. */
+int32_t dsa_abi_version(void);
+
+/* Bytes of workspace the matching call needs (0 is possible). Validates the
+ * shape fields only; pointers may be NULL. */
+dsa_status dsa_indexer_workspace_size(const dsa_indexer_args *args, size_t *bytes);
+dsa_status dsa_attn_workspace_size(const dsa_attn_args *args, size_t *bytes);
+dsa_status dsa_stack_workspace_size(const dsa_stack_args *args, size_t *bytes);
+
+/* Resolves the IndexCache layer pattern (README, Options A and B and Default
+ * behavior) into out[0..n_layers) of 'F'/'S' plus a terminating NUL (out is a
+ * HOST buffer of n_layers + 1 bytes). Rules:
+ *   pattern != NULL: length n_layers, characters 'F'/'S' only (case
+ *                    sensitive), first character 'F'   -> else BAD_PATTERN
+ *   index_topk_freq > 0: layer l is F iff l % freq == 0 (layer 0 is F)
+ *   neither set: every layer is F
+ *   both set, freq < 0 or n_layers < 1: INVALID_ARGUMENT.
+ * Pure host code; needs no GPU. */
+dsa_status dsa_resolve_pattern(int32_t n_layers, const char *pattern, int32_t index_topk_freq,
+                               char *out);
+
+/* The indexer scores of every causal (query, key) pair followed by the exact
+ * per-query top-k of those scores (rank order, -1 padded). The L x L score
+ * matrix is never stored (except in debug_full_scores test mode). */
+dsa_status dsa_indexer_scores_topk(const dsa_indexer_args *args, void *stream);
+
+/* Softmax attention of every query head over the key/value rows listed in idx. */
+dsa_status dsa_sparse_attn(const dsa_attn_args *args, void *stream);
+
+/* Runs the layer stack: layer l runs the indexer into idx_buf iff the resolved
+ * pattern (pattern string, or index_topk_freq, or neither = all F) has 'F' at
+ * l, then sparse attention of layer l over idx_buf. Arguments are validated
+ * for every layer before anything is enqueued. */
+dsa_status dsa_layer_stack_run(const dsa_stack_args *args, const char *pattern,
+                               int32_t index_topk_freq, void *stream);
+
+/* Static text of a status code. */
+const char *dsa_status_string(dsa_status status);
+
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char *dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,189 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/dsa.h declares, resolves patterns like the oracle, and rejects invalid
+arguments on the host before any HIP call (outputs untouched)."""
+import ctypes
+import os
+import random
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from oracle import PatternError
+import dsa_indexer_top_amd as dsa
+from dsa_indexer_top_amd import _lib as L
+from dsa_indexer_top_amd.api import attn_args, indexer_args
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dsa.load()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(L.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.dsa_abi_version() == 1
+
+
+def _c_layout(tmp_path, struct, fields):
+    """sizeof/offsetof of a dsa.h struct as the C compiler lays it out."""
+    src = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "dsa.h"', "int main(void){",
+             f'printf("%zu\\n", sizeof({struct}));']
+    lines += [f'printf("%zu\\n", offsetof({struct}, {f}));' for f in fields]
+    lines.append("return 0;}")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    return [int(x) for x in out]
+
+
+@pytest.mark.parametrize("cls,struct", [(L.IndexerArgs, "dsa_indexer_args"),
+                                        (L.AttnArgs, "dsa_attn_args"),
+                                        (L.StackArgs, "dsa_stack_args")])
+def test_ctypes_layout_matches_header(tmp_path, cls, struct):
+    fields = [f for f, _ in cls._fields_]
+    got = [ctypes.sizeof(cls)] + [getattr(cls, f).offset for f in fields]
+    assert got == _c_layout(tmp_path, struct, fields)
+
+
+def test_status_strings(lib):
+    assert lib.dsa_status_string(0) == b"DSA_OK"
+    assert lib.dsa_status_string(3) == b"DSA_ERR_BAD_PATTERN"
+
+
+def test_pattern_resolution_matches_oracle():
+    rng = random.Random(4)
+    cases = [(47, None, 0), (47, None, 2), (47, None, 4), (47, None, 1), (5, None, 7),
+             (78, "FFSFSSSFSSFFFSSSFFFSFSSSSSSFFSFFSFFSSFFFFFFSFFFFFSFFSSSSSSFSFFFSFSSSFSFFSFFSSS", 0)]
+    for _ in range(30):
+        n = rng.randint(1, 60)
+        cases.append((n, "F" + "".join(rng.choice("FS") for _ in range(n - 1)), 0))
+    for n, pat, freq in cases:
+        assert dsa.resolve_pattern(n, pat, freq) == oracle.resolve_pattern(n, pat, freq)
+
+
+@pytest.mark.parametrize("n,pat,freq,status", [
+    (4, "FSF", 0, L.DSA_ERR_BAD_PATTERN),
+    (4, "FSFSF", 0, L.DSA_ERR_BAD_PATTERN),
+    (4, "FSXF", 0, L.DSA_ERR_BAD_PATTERN),
+    (4, "fsfs", 0, L.DSA_ERR_BAD_PATTERN),
+    (4, "SFFF", 0, L.DSA_ERR_BAD_PATTERN),
+    (4, "FSFS", 2, L.DSA_ERR_INVALID_ARGUMENT),
+    (4, None, -1, L.DSA_ERR_INVALID_ARGUMENT),
+    (0, None, 0, L.DSA_ERR_INVALID_ARGUMENT),
+])
+def test_pattern_errors(n, pat, freq, status):
+    with pytest.raises(dsa.DsaError) as ei:
+        dsa.resolve_pattern(n, pat, freq)
+    assert ei.value.status == status
+    with pytest.raises(PatternError):
+        oracle.resolve_pattern(n, pat, freq)
+
+
+FAKE = 0x10000  # aligned non-NULL address; never dereferenced (validation fails first)
+
+
+def _idx_args(**kw):
+    d = dict(B=1, n_q=64, n_k=64, pos_offset=0, H=64, D=128, topk=16, code=L.DSA_BF16)
+    d.update(kw)
+    a = indexer_args(d["B"], d["n_q"], d["n_k"], d["pos_offset"], d["H"], d["D"], d["topk"], d["code"])
+    a.q = a.k = a.w = a.out_idx = FAKE
+    return a
+
+
+def _call_idx(lib, a):
+    return lib.dsa_indexer_scores_topk(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("mut,status", [
+    (lambda a: setattr(a, "struct_size", 8), L.DSA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "q", None), L.DSA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "out_idx", None), L.DSA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "k", FAKE + 8), L.DSA_ERR_INVALID_ARGUMENT),        # misaligned
+    (lambda a: setattr(a, "n_q", 0), L.DSA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "q_pos_offset", 1), L.DSA_ERR_INVALID_ARGUMENT),    # offset + n_q > n_k
+    (lambda a: setattr(a, "q_pos_offset", -1), L.DSA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "head_dim", 96), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "n_heads", 65), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "topk", 0), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "topk", 2049), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "dtype", 7), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "q_scale", FAKE), L.DSA_ERR_INVALID_ARGUMENT),      # scales with bf16
+    (lambda a: (setattr(a, "dtype", L.DSA_FP8_E4M3FN), setattr(a, "head_dim", 32)), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "dtype", L.DSA_FP8_E4M3FN), L.DSA_ERR_INVALID_ARGUMENT),  # fp8 without scales
+    (lambda a: None, L.DSA_ERR_WORKSPACE),                                       # no workspace
+    (lambda a: (setattr(a, "workspace", FAKE), setattr(a, "workspace_bytes", 100)), L.DSA_ERR_WORKSPACE),
+    (lambda a: (setattr(a, "B", 70000)), L.DSA_ERR_INVALID_ARGUMENT),
+])
+def test_indexer_validation(lib, mut, status):
+    a = _idx_args()
+    mut(a)
+    assert _call_idx(lib, a) == status
+    assert lib.dsa_last_error() != b""
+
+
+def test_size_overflow_rejected(lib):
+    a = _idx_args(B=65535, n_q=2 ** 31 - 1, n_k=2 ** 31 - 1, H=64, D=128)
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_indexer_workspace_size(ctypes.byref(a), ctypes.byref(n)) == L.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_size_is_reported():
+    n = dsa.indexer_workspace_size(1, 1024, 1024, 64, 128, 2048)
+    assert n >= 2 * 1024 * 4096 * 4
+    assert dsa.indexer_workspace_size(2, 1, 5000, 64, 128, 2048) > 2 * 5000 * 4
+    assert dsa.attn_workspace_size(1, 1024, 1024, 16, 128, 2048) == 0       # prefill: none
+    assert dsa.attn_workspace_size(2, 1, 5000, 16, 128, 2048) > 0          # decode split partials
+
+
+@pytest.mark.parametrize("mut,status", [
+    (lambda a: setattr(a, "n_heads", 17), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "head_dim", 32), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "topk", 4097), L.DSA_ERR_UNSUPPORTED),
+    (lambda a: setattr(a, "scale", -1.0), L.DSA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "scale", float("nan")), L.DSA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "idx", None), L.DSA_ERR_INVALID_ARGUMENT),
+    (lambda a: setattr(a, "v", FAKE + 4), L.DSA_ERR_INVALID_ARGUMENT),
+])
+def test_attn_validation(lib, mut, status):
+    a = attn_args(1, 64, 64, 0, 16, 128, 64, 0.0)
+    a.q = a.k = a.v = a.idx = a.out = FAKE
+    mut(a)
+    assert lib.dsa_sparse_attn(ctypes.byref(a), None) == status
+
+
+def test_stack_validation(lib):
+    a = L.StackArgs()
+    a.struct_size = ctypes.sizeof(L.StackArgs)
+    a.n_layers = 4
+    a.indexer = indexer_args(1, 64, 64, 0, 4, 32, 16, L.DSA_BF16)
+    a.attn = attn_args(1, 64, 64, 0, 4, 64, 16, 0.0)
+    # bad pattern is reported before anything else is looked at
+    assert lib.dsa_layer_stack_run(ctypes.byref(a), b"SFFF", 0, None) == L.DSA_ERR_BAD_PATTERN
+    assert lib.dsa_layer_stack_run(ctypes.byref(a), b"FSFS", 2, None) == L.DSA_ERR_INVALID_ARGUMENT
+    # missing per-layer arrays
+    assert lib.dsa_layer_stack_run(ctypes.byref(a), b"FSFS", 0, None) == L.DSA_ERR_INVALID_ARGUMENT
+    # shapes that disagree between indexer and attention
+    a.attn = attn_args(1, 64, 64, 0, 4, 64, 32, 0.0)
+    assert lib.dsa_layer_stack_run(ctypes.byref(a), None, 0, None) == L.DSA_ERR_INVALID_ARGUMENT
+    # the workspace does not depend on the pattern: its size call takes none
+    a.attn = attn_args(1, 64, 64, 0, 4, 64, 16, 0.0)
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_stack_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value == max(dsa.indexer_workspace_size(1, 64, 64, 4, 32, 16),
+                          dsa.attn_workspace_size(1, 64, 64, 4, 64, 16))

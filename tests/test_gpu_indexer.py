@@ -1,0 +1,117 @@
+"""GPU parity of dsa_indexer_scores_topk against the CPU oracle (prefill and decode)."""
+import numpy as np
+import pytest
+import torch
+
+from dsa_inputs import make_indexer_inputs, make_int_indexer_inputs
+from _gpu_helpers import check_indexer, overlap, run_indexer, say
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ prefill
+@pytest.mark.parametrize("shape,topk", [
+    ((1, 256, 256, 4, 32), 16),      # tiny stack layer shape
+    ((1, 300, 300, 64, 128), 64),    # two head blocks, ragged last tile
+    ((2, 97, 97, 20, 64), 8),        # heads not a multiple of 32, B = 2
+])
+def test_prefill_exact_integer(dsa, shape, topk):
+    say(f"prefill exact {shape} k={topk}")
+    inp = make_int_indexer_inputs(*shape, seed=11)
+    check_indexer(dsa, inp, topk, exact=True)
+
+
+@pytest.mark.parametrize("shape,topk,cfg", [
+    ((1, 256, 256, 4, 32), 16, 1),
+    ((1, 1000, 1000, 64, 128), 64, 2),     # many in-kernel compactions (capacity 192)
+    ((1, 333, 333, 64, 64), 300, 3),       # k close to L
+    ((1, 2, 2, 64, 128), 16, 4),           # smallest prefill
+    ((1, 130, 700, 64, 128), 32, 5),       # chunked prefill: queries are the last 130 of 700
+])
+def test_prefill_random_bf16(dsa, shape, topk, cfg):
+    say(f"prefill bf16 {shape} k={topk}")
+    inp = make_indexer_inputs(*shape, config=cfg)
+    check_indexer(dsa, inp, topk)
+
+
+def test_prefill_k2048_compaction(dsa):
+    """k = 2048 with rows longer than the 4096-entry candidate list, so the exact
+    in-kernel compaction runs; sampled rows incl. the first compacting ones."""
+    L = 4700
+    say(f"prefill bf16 L={L} k=2048")
+    inp = make_indexer_inputs(1, L, L, 64, 128, config=6, w_std=0.125)
+    rows = [0, 1, 2046, 2047, 2048, 2049, 4030, 4031, 4032, 4033, 4095, 4096, 4200, L - 2, L - 1]
+    rows += list(np.random.default_rng(0).choice(L, 25, replace=False))
+    check_indexer(dsa, inp, 2048, rows=sorted(set(int(r) for r in rows)))
+
+
+def test_prefill_all_ties(dsa):
+    """q = 0: every score is 0, so each row must list its first min(k, t+1)
+    tokens in index order (tie rule through many compactions)."""
+    say("prefill all ties")
+    inp = make_indexer_inputs(1, 700, 700, 8, 64, config=7)
+    inp.q.zero_()
+    r, _ = check_indexer(dsa, inp, 64, exact=True)
+    idx = r.idx.cpu().numpy()[0]
+    for t in (0, 5, 63, 64, 699):
+        n = min(64, t + 1)
+        assert idx[t, :n].tolist() == list(range(n))
+
+
+@pytest.mark.parametrize("exact", [True, False])
+def test_prefill_fp8(dsa, exact):
+    say(f"prefill fp8 exact={exact}")
+    if exact:
+        inp = make_int_indexer_inputs(1, 300, 300, 64, 128, seed=12, dtype="fp8")
+    else:
+        inp = make_indexer_inputs(1, 300, 300, 64, 128, config=8, dtype="fp8")
+    check_indexer(dsa, inp, 64, exact=exact)
+
+
+def test_prefill_fp8_d64(dsa):
+    say("prefill fp8 D=64")
+    inp = make_indexer_inputs(1, 200, 200, 16, 64, config=9, dtype="fp8")
+    check_indexer(dsa, inp, 32)
+
+
+def test_prefill_dump_mode_does_not_change_result(dsa):
+    inp = make_indexer_inputs(1, 600, 600, 64, 128, config=10)
+    a = run_indexer(dsa, inp, 128, dump=True)
+    b = run_indexer(dsa, inp, 128, dump=False)
+    c = run_indexer(dsa, inp, 128, dump=False)
+    assert torch.equal(a.idx, b.idx) and torch.equal(b.idx, c.idx)
+    assert torch.equal(a.scores.view(torch.int32), b.scores.view(torch.int32))
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("B,n_k,topk,cfg", [
+    (3, 5000, 2048, 20),
+    (1, 777, 64, 21),
+    (2, 100, 2048, 22),   # fewer keys than k: -1 padding
+])
+def test_decode_random_bf16(dsa, B, n_k, topk, cfg):
+    say(f"decode bf16 B={B} n_k={n_k} k={topk}")
+    inp = make_indexer_inputs(B, 1, n_k, 64, 128, config=cfg, w_std=0.125)
+    check_indexer(dsa, inp, topk)
+
+
+def test_decode_exact_integer(dsa):
+    say("decode exact")
+    inp = make_int_indexer_inputs(2, 1, 3000, 64, 128, seed=13)
+    check_indexer(dsa, inp, 100, exact=True)
+
+
+def test_decode_all_ties_overflow_path(dsa):
+    """All scores equal: the candidate list overflows and the exact full-row
+    select must return the k lowest indices in order."""
+    say("decode all ties")
+    inp = make_indexer_inputs(1, 1, 9000, 64, 128, config=23)
+    inp.q.zero_()
+    r, _ = check_indexer(dsa, inp, 2048, exact=True)
+    assert r.idx.cpu().numpy()[0, 0].tolist() == list(range(2048))
+
+
+def test_decode_fp8(dsa):
+    say("decode fp8")
+    inp = make_indexer_inputs(2, 1, 4000, 64, 128, config=24, dtype="fp8")
+    check_indexer(dsa, inp, 512)
