@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA indexer + top-k hot path on one MI355X.
+
+Headline (the JSON line's `value`): single-layer prefill lightning indexer fused
+with exact top-k at L = 200000 tokens, H_I = 64 indexer heads, d_I = 128,
+top-k = 2048, fp8 e4m3 q_idx/k_idx with per-token fp32 scales (causal). A step
+is one dsa_indexer_scores_topk call over the whole layer (score kernel +
+selection kernel) with inputs resident in HBM; value = L / step time.
+
+`roofline` is for the dominant kernel (the fused score + streaming-filter
+kernel): its algorithmic work is L(L+1)/2 * H_I * d_I * 2 flop per launch (the
+causal triangle only), timed live with HIP events recorded by the library on
+the stream it launches on. `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same layer's query rows and extrapolates by the number of
+causal keys. `extra` adds the bf16 200K layer, the 47-layer F/S prefill stack at
+L = 61440 (all-F, index_topk_freq 2 and 4) and decode at 200K context.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer+top-k queries/sec & fraction of MFMA peak at 200K; stack prefill time F/S"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_prefill_fp8_L200000_traffic.json")
+KERNEL_SOURCES = ["dsa_indexer_top_amd/csrc/indexer_prefill.hip", "dsa_indexer_top_amd/csrc/dsa_device.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def causal_flops(L, H, D):
+    return L * (L + 1) // 2 * H * D * 2
+
+
+def time_indexer(dsa, torch, inp, topk, steps, warmup):
+    """Returns (ms per step wall-clock, mean score-kernel ms, mean select ms, idx)."""
+    g = inp
+    B, n_q, H, D = g.q.shape
+    n_k = g.k.shape[1]
+    code = 1 if g.dtype == "fp8" else 0
+    ws = torch.empty(dsa.indexer_workspace_size(B, n_q, n_k, H, D, topk, code), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((B, n_q, topk), dtype=torch.int32, device="cuda")
+    call = lambda ev=None: dsa.indexer_scores_topk(g.q, g.k, g.w, topk, q_scale=g.q_scale,
+                                                   k_scale=g.k_scale, pos_offset=g.pos_offset,
+                                                   out_idx=out, workspace=ws, phase_events=ev)
+    for _ in range(warmup):
+        call()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    s_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    del ws
+    return wall, k_ms, s_ms, out
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per launch of the score kernel from the committed rocprofv3
+    counter summary, or None if the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(inp_host, L, topk, budget_s):
+    """Times the fp64 oracle on seeded random query rows of the layer until the
+    time budget is spent, and extrapolates to the whole layer by causal keys."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    rng = np.random.default_rng(2024)
+    order = rng.permutation(L)
+    done_rows, done_keys, spent = 0, 0, 0.0
+    q, k, w, qs, ks, dt = inp_host
+    i = 0
+    while spent < budget_s and i < L:
+        rows = sorted(int(r) for r in order[i:i + 4])
+        i += 4
+        t0 = time.perf_counter()
+        sc = oracle.indexer_scores_rows(q, k, w, rows, dtype=dt, q_scale=qs, k_scale=ks)
+        oracle.topk_from_scores(sc, topk, rows=rows)
+        spent += time.perf_counter() - t0
+        done_rows += len(rows)
+        done_keys += sum(r + 1 for r in rows)
+    total_keys = L * (L + 1) // 2
+    est_s = spent / done_keys * total_keys
+    return {"value": L / est_s, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{done_rows} seeded-random query rows of the same layer ({done_keys} causal "
+                       f"keys, {spent:.1f} s of fp64 oracle: scores + top-k), extrapolated to all "
+                       f"{L} rows by causal-key count (layer estimate {est_s:.0f} s)")}
+
+
+def stack_bench(dsa, torch, L, n_layers, topk, steps, warmup, config=3):
+    """47-layer prefill stack, per-layer tensors seeded independently, one shared
+    index buffer; all-F vs index_topk_freq 2 vs 4."""
+    from dsa_inputs import make_attn_inputs, make_indexer_inputs
+    layers = []
+    for l in range(n_layers):
+        ii = make_indexer_inputs(1, L, L, 64, 128, config=config, layer=l, w_std=0.125, device="cuda")
+        aa = make_attn_inputs(1, L, L, 16, 128, config=config, layer=l, device="cuda")
+        layers.append(dict(q_idx=ii.q, k_idx=ii.k, w=ii.w, q_scale=None, k_scale=None,
+                           q=aa.q, k=aa.k, v=aa.v))
+    st = dsa.LayerStack(layers, topk, shared_out=True, events=True)
+    res = {}
+    for name, kw in (("all_F", {}), ("freq2", {"freq": 2}), ("freq4", {"freq": 4})):
+        for _ in range(warmup):
+            st.run(**kw)
+        torch.cuda.synchronize()
+        times, per_layer = [], None
+        for _ in range(steps):
+            t0 = time.perf_counter()
+            st.run(**kw)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+            per_layer = st.layer_times_ms()
+        pat = dsa.resolve_pattern(n_layers, None, kw.get("freq", 0))
+        f_ms = [t for t, c in zip(per_layer, pat) if c == "F"]
+        s_ms = [t for t, c in zip(per_layer, pat) if c == "S"]
+        res[name] = {"pattern_F": pat.count("F"), "time_s": min(times),
+                     "mean_F_layer_ms": sum(f_ms) / len(f_ms),
+                     "mean_S_layer_ms": (sum(s_ms) / len(s_ms)) if s_ms else None}
+        log(f"stack {name}: {min(times):.3f} s")
+    for name in ("freq2", "freq4"):
+        res[name]["speedup_vs_all_F"] = res["all_F"]["time_s"] / res[name]["time_s"]
+    del st, layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, config=4):
+    """One decode token over n_layers with a seeded 12-F pattern; independent
+    caches per request. B = 1 uses distinct tensors for every layer; larger B
+    rotates two distinct layer sets (each far larger than the 256 MB MALL)."""
+    from dsa_inputs import make_attn_inputs, make_indexer_inputs, seeded_pattern
+    n_sets = n_layers if B == 1 else 2
+    sets = []
+    for l in range(n_sets):
+        ii = make_indexer_inputs(B, 1, T, 64, 128, config=config, layer=l, w_std=0.125, device="cuda")
+        aa = make_attn_inputs(B, 1, T, 16, 128, config=config, layer=l, device="cuda")
+        sets.append(dict(q_idx=ii.q, k_idx=ii.k, w=ii.w, q_scale=None, k_scale=None,
+                         q=aa.q, k=aa.k, v=aa.v))
+    layers = [sets[l % n_sets] for l in range(n_layers)]
+    pat = seeded_pattern(n_layers, 12, seed=1_000_000 * config + 9)
+    # per-kernel HBM rates on one layer
+    l0 = sets[0]
+    evi = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    eva = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    k_ms = a_ms = 0.0
+    idx = None
+    for i in range(warmup + steps):
+        r = dsa.indexer_scores_topk(l0["q_idx"], l0["k_idx"], l0["w"], topk, phase_events=evi)
+        idx = r.idx
+        dsa.sparse_attn(l0["q"], l0["k"], l0["v"], idx, phase_events=eva)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            k_ms += evi[0].elapsed_time(evi[1]) / steps
+            a_ms += eva[0].elapsed_time(eva[1]) / steps
+    idx_bytes = B * T * 128 * 2 + B * T * 4                 # k_idx read + score keys written
+    att_bytes = B * topk * 2 * 128 * 2                      # gathered K and V rows
+    st = dsa.LayerStack(layers, topk, shared_out=True)
+    for _ in range(warmup):
+        st.run(pat)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        st.run(pat)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    step = min(times)
+    res = {"B": B, "context": T, "pattern": pat,
+           "indexer_kernel_ms": k_ms, "indexer_hbm_GBps": idx_bytes / k_ms / 1e6,
+           "indexer_hbm_frac": idx_bytes / k_ms / 1e6 / PEAK_HBM_GBS,
+           "attn_ms": a_ms, "attn_gather_GBps": att_bytes / a_ms / 1e6,
+           "step_ms_47_layers": step * 1e3, "tok_per_s_per_request": 1.0 / step,
+           "tok_per_s_total": B / step}
+    log(f"decode B={B}: indexer {k_ms:.3f} ms ({res['indexer_hbm_GBps']:.0f} GB/s), "
+        f"attn {a_ms:.3f} ms, 47-layer step {step*1e3:.2f} ms")
+    del st, layers, sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--L", type=int, default=200000)
+    ap.add_argument("--dtype", default="fp8", choices=["fp8", "bf16"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="headline only")
+    ap.add_argument("--quick", action="store_true", help="headline + CPU baseline only")
+    ap.add_argument("--stack-L", type=int, default=61440)
+    ap.add_argument("--stack-layers", type=int, default=47)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; --gpus N > 1 (or WORLD_SIZE > 1) is not "
+              "supported (the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dsa_indexer_top_amd as dsa
+    from dsa_inputs import host_bits, make_indexer_inputs
+    dsa.load()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    L, H, D, topk = args.L, 64, 128, 2048
+
+    log(f"generating the L={L} {args.dtype} layer")
+    inp = make_indexer_inputs(1, L, L, H, D, config=5, dtype=args.dtype, w_std=0.125, device="cuda")
+    torch.cuda.synchronize()
+    log("timing the headline")
+    wall_ms, k_ms, s_ms, _ = time_indexer(dsa, torch, inp, topk, args.steps, args.warmup)
+    flops = causal_flops(L, H, D)
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    log(f"headline: {wall_ms:.2f} ms/step, score kernel {k_ms:.2f} ms ({achieved:.1f} TFLOP/s), "
+        f"select {s_ms:.2f} ms")
+    result = {
+        "metric": METRIC,
+        "value": L / (wall_ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic: seeded N(0,1) q_idx/k_idx"
+                + (" clipped to +-8 and cast to e4m3 with per-token fp32 scales U[0.5,2)"
+                   if args.dtype == "fp8" else " in bf16") + ", w ~ N(0,1)/8",
+        "config": {"workload": f"single-layer prefill indexer + exact top-k, L={L}, H_I={H}, d_I={D}, "
+                               f"k={topk}, causal, {args.dtype}",
+                   "L": L, "H_I": H, "d_I": D, "topk": topk},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS[args.dtype],
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS[args.dtype],
+                     "traffic": traffic_for_current_kernel() if (args.dtype == "fp8" and L == 200000)
+                     else None,
+                     "kernel": "indexer_prefill_kernel", "kernel_ms": k_ms,
+                     "flop_per_launch": flops},
+        "select_kernel_ms": s_ms,
+    }
+    if not args.no_cpu:
+        log("CPU oracle baseline")
+        hb = (host_bits(inp.q[:, :]), host_bits(inp.k), host_bits(inp.w), host_bits(inp.q_scale),
+              host_bits(inp.k_scale), inp.dtype)
+        result["cpu_baseline"] = cpu_baseline(hb, L, topk, args.cpu_seconds)
+    del inp
+    torch.cuda.empty_cache()
+
+    if not (args.no_extra or args.quick):
+        extra = {}
+        other = "bf16" if args.dtype == "fp8" else "fp8"
+        log(f"generating the L={L} {other} layer")
+        inp2 = make_indexer_inputs(1, L, L, H, D, config=5, dtype=other, w_std=0.125, device="cuda")
+        w2, k2, s2, _ = time_indexer(dsa, torch, inp2, topk, max(2, args.steps // 2), 1)
+        a2 = flops / (k2 * 1e-3) / 1e12
+        extra[f"{other}_L{L}"] = {"ms_per_step": w2, "queries_per_s": L / (w2 * 1e-3),
+                                  "score_kernel_ms": k2, "select_kernel_ms": s2,
+                                  "TFLOPs": a2, "mfma_frac": a2 / PEAK_TFLOPS[other],
+                                  "frac_of_bf16_peak": a2 / PEAK_TFLOPS["bf16"]}
+        log(f"{other}: {w2:.2f} ms/step, kernel {k2:.2f} ms ({a2:.1f} TFLOP/s)")
+        del inp2
+        torch.cuda.empty_cache()
+        log(f"stack prefill L={args.stack_L}, {args.stack_layers} layers")
+        extra["stack_prefill"] = {"L": args.stack_L, "layers": args.stack_layers, "dtype": "bf16",
+                                  "attn": "16 heads, d=128, 1 KV head",
+                                  **stack_bench(dsa, torch, args.stack_L, args.stack_layers, topk,
+                                                max(1, args.steps // 2), 1)}
+        for B in (1, 32):
+            log(f"decode B={B}")
+            extra[f"decode_B{B}"] = decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
+        result["extra"] = extra
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

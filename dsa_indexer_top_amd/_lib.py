@@ -42,6 +42,7 @@ class IndexerArgs(ctypes.Structure):
         ("q_scale", c_void_p), ("k_scale", c_void_p),
         ("out_idx", c_void_p), ("out_scores", c_void_p), ("debug_full_scores", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+        ("phase_events", c_void_p),
     ]
 
 
@@ -54,6 +55,7 @@ class AttnArgs(ctypes.Structure):
         ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("idx", c_void_p),
         ("out", c_void_p), ("lse", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+        ("phase_events", c_void_p),
     ]
 
 

@@ -135,7 +135,7 @@ def indexer_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk:
                         out_idx: Optional[torch.Tensor] = None,
                         out_scores=False, debug_full_scores=False,
                         workspace: Optional[torch.Tensor] = None,
-                        stream=None) -> IndexerResult:
+                        stream=None, phase_events=None) -> IndexerResult:
     """Lightning-indexer scores + exact per-query top-k (dsa_indexer_scores_topk).
 
     q [B, n_q, H, D], k [B, n_k, D] (bf16 or float8_e4m3fn), w [B, n_q, H] fp32,
@@ -185,6 +185,8 @@ def indexer_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk:
     a.out_idx, a.out_scores, a.debug_full_scores = _ptr(out_idx), _ptr(sc), _ptr(full)
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    keep = _event_array(phase_events, 3)
+    a.phase_events = None if keep is None else ctypes.cast(keep, ctypes.c_void_p)
     _check(L.load().dsa_indexer_scores_topk(ctypes.byref(a), _stream(stream)))
     return IndexerResult(out_idx, sc, full)
 
@@ -192,7 +194,7 @@ def indexer_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk:
 def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, *,
                 scale: float = 0.0, pos_offset: Optional[int] = None,
                 out: Optional[torch.Tensor] = None, lse=False,
-                workspace: Optional[torch.Tensor] = None, stream=None):
+                workspace: Optional[torch.Tensor] = None, stream=None, phase_events=None):
     """Sparse attention (dsa_sparse_attn): q [B, n_q, H, D], k/v [B, n_k, D] bf16,
     idx [B, n_q, topk] int32. Returns (out bf16 [B, n_q, H, D], lse or None)."""
     _need(q, "q", dtype=torch.bfloat16, ndim=4)
@@ -225,8 +227,24 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Te
     a.q, a.k, a.v, a.idx, a.out, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out), _ptr(lse_t)
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    keep = _event_array(phase_events, 2)
+    a.phase_events = None if keep is None else ctypes.cast(keep, ctypes.c_void_p)
     _check(L.load().dsa_sparse_attn(ctypes.byref(a), _stream(stream)))
     return out, lse_t
+
+
+def _event_array(events, n):
+    """Host array of hipEvent_t handles from torch.cuda.Event objects (or None)."""
+    if events is None:
+        return None
+    if len(events) != n:
+        raise ValueError(f"phase_events needs {n} events")
+    arr = (ctypes.c_void_p * n)()
+    for i, e in enumerate(events):
+        if e.cuda_event == 0:   # torch creates the underlying event lazily
+            e.record()
+        arr[i] = e.cuda_event
+    return arr
 
 
 def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):
@@ -290,12 +308,7 @@ class LayerStack:
         self.events = None
         if events:
             self.events = [torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)]
-            # torch.cuda.Event creates its hipEvent lazily; record once to materialise it.
-            for e in self.events:
-                e.record()
-            ev = (ctypes.c_void_p * len(self.events))()
-            for i, e in enumerate(self.events):
-                ev[i] = e.cuda_event
+            ev = _event_array(self.events, len(self.events))
             self._keep.append(ev)
             a.layer_events = ctypes.cast(ev, ctypes.c_void_p)
         n = ctypes.c_size_t(0)

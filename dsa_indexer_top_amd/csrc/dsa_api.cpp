@@ -146,6 +146,7 @@ dsa::IndexerParams make_indexer_params(const dsa_indexer_args* a, const void* q,
   p.out_idx = out_idx;
   p.out_scores = out_scores;
   p.dump = dump;
+  p.ev = nullptr;
   dsa::indexer_bind_workspace(p, ws);
   return p;
 }
@@ -170,6 +171,7 @@ dsa::AttnParams make_attn_params(const dsa_attn_args* a, const void* q, const vo
   p.lse = lse;
   p.nsplit = dsa::attn_nsplit(a->B, a->n_q, a->topk);
   p.part = (float*)ws;
+  p.ev = nullptr;
   return p;
 }
 
@@ -338,8 +340,9 @@ dsa_status dsa_indexer_scores_topk(const dsa_indexer_args* a, void* stream) {
   const size_t need = dsa::indexer_workspace_bytes(a->B, a->n_q, a->n_k, a->topk);
   st = check_workspace(a->workspace, a->workspace_bytes, need, what);
   if (st != DSA_OK) return st;
-  const dsa::IndexerParams p = make_indexer_params(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx,
-                                                   a->out_scores, a->debug_full_scores, a->workspace);
+  dsa::IndexerParams p = make_indexer_params(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx,
+                                             a->out_scores, a->debug_full_scores, a->workspace);
+  p.ev = a->phase_events;
   st = run_indexer(p, (hipStream_t)stream);
   return st == DSA_OK ? ok() : st;
 }
@@ -353,7 +356,8 @@ dsa_status dsa_sparse_attn(const dsa_attn_args* a, void* stream) {
   const size_t need = dsa::attn_workspace_bytes(a->B, a->n_q, a->n_k, a->n_heads, a->head_dim, a->topk);
   st = check_workspace(a->workspace, a->workspace_bytes, need, what);
   if (st != DSA_OK) return st;
-  const dsa::AttnParams p = make_attn_params(a, a->q, a->k, a->v, a->idx, a->out, a->lse, a->workspace);
+  dsa::AttnParams p = make_attn_params(a, a->q, a->k, a->v, a->idx, a->out, a->lse, a->workspace);
+  p.ev = a->phase_events;
   st = run_attn(p, (hipStream_t)stream);
   return st == DSA_OK ? ok() : st;
 }

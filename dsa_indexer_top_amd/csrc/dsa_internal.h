@@ -39,7 +39,13 @@ struct IndexerParams {
   int C;
   uint32_t* dec_keys;   // decode: [B, n_k] score keys
   uint32_t* dec_hist;   // decode: [B, kDecodeHistBins]
+  void* const* ev;      // optional phase events (3): before scores, after scores, after select
 };
+
+// Records phase event i (if any) on the stream.
+inline hipError_t record_phase(void* const* ev, int i, hipStream_t s) {
+  return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
+}
 
 struct AttnParams {
   int B, n_q, n_k, pos_offset, H, D, topk;
@@ -52,6 +58,7 @@ struct AttnParams {
   float* lse;
   int nsplit;           // >1: split-K over the idx list (decode), partials in ws
   float* part;          // [rows, nsplit, H, D + 2]
+  void* const* ev;      // optional phase events (2): before, after
 };
 
 size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk);

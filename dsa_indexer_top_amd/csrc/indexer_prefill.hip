@@ -313,7 +313,9 @@ static hipError_t launch_prefill_t(const IndexerParams& p, hipStream_t s) {
 hipError_t launch_topk_finalize(const IndexerParams& p, int rows, hipStream_t s);
 
 hipError_t launch_indexer_prefill(const IndexerParams& p, hipStream_t s) {
-  hipError_t e = hipErrorInvalidValue;
+  hipError_t e = record_phase(p.ev, 0, s);
+  if (e != hipSuccess) return e;
+  e = hipErrorInvalidValue;
   const bool two = p.H > 32;
   if (p.fp8) {
     if (p.D == 64) e = two ? launch_prefill_t<64, 2, true>(p, s) : launch_prefill_t<64, 1, true>(p, s);
@@ -324,7 +326,11 @@ hipError_t launch_indexer_prefill(const IndexerParams& p, hipStream_t s) {
     else if (p.D == 128) e = two ? launch_prefill_t<128, 2, false>(p, s) : launch_prefill_t<128, 1, false>(p, s);
   }
   if (e != hipSuccess) return e;
-  return launch_topk_finalize(p, p.B * p.n_q, s);
+  e = record_phase(p.ev, 1, s);
+  if (e != hipSuccess) return e;
+  e = launch_topk_finalize(p, p.B * p.n_q, s);
+  if (e != hipSuccess) return e;
+  return record_phase(p.ev, 2, s);
 }
 
 }  // namespace dsa

@@ -218,9 +218,13 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s) {
 }
 
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s) {
-  if (p.D == 64) return launch_attn_t<64>(p, s);
-  if (p.D == 128) return launch_attn_t<128>(p, s);
-  return hipErrorInvalidValue;
+  hipError_t e = record_phase(p.ev, 0, s);
+  if (e != hipSuccess) return e;
+  if (p.D == 64) e = launch_attn_t<64>(p, s);
+  else if (p.D == 128) e = launch_attn_t<128>(p, s);
+  else e = hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  return record_phase(p.ev, 1, s);
 }
 
 }  // namespace dsa

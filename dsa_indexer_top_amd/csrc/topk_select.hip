@@ -404,6 +404,8 @@ hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, s, p.dec_hist, nh, 0u);
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((p.B + 255) / 256)), dim3(256), 0, s,
                      (uint32_t*)p.cand_cnt, (size_t)p.B, 0u);
+  hipError_t e = record_phase(p.ev, 0, s);
+  if (e != hipSuccess) return e;
   const bool two = p.H > 32;
   if (p.fp8) {
     if (p.D == 64) two ? launch_decode_scores_t<64, 2, true>(p, s) : launch_decode_scores_t<64, 1, true>(p, s);
@@ -413,12 +415,16 @@ hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
     else if (p.D == 64) two ? launch_decode_scores_t<64, 2, false>(p, s) : launch_decode_scores_t<64, 1, false>(p, s);
     else two ? launch_decode_scores_t<128, 2, false>(p, s) : launch_decode_scores_t<128, 1, false>(p, s);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = record_phase(p.ev, 1, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_collect_kernel, dim3(kDecodeCollectBlocks, p.B), dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_finalize(p, p.B, s);
+  e = launch_topk_finalize(p, p.B, s);
+  if (e != hipSuccess) return e;
+  return record_phase(p.ev, 2, s);
 }
 
 }  // namespace dsa

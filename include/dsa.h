@@ -105,6 +105,11 @@ typedef struct {
   float *debug_full_scores;
   void *workspace;
   size_t workspace_bytes;
+  /* Optional (NULL): HOST array of 3 hipEvent_t (as void*) recorded on the
+   * stream before the score kernel, between the score kernel and the
+   * selection kernels, and after the last kernel, so that a caller can time
+   * the phases without a profiler. */
+  void *const *phase_events;
 } dsa_indexer_args;
 
 /* Sparse attention over given indices, one KV head shared by n_heads query
@@ -131,13 +136,16 @@ typedef struct {
   float *lse;
   void *workspace;
   size_t workspace_bytes;
+  /* Optional (NULL): HOST array of 2 hipEvent_t recorded before the first and
+   * after the last attention kernel. */
+  void *const *phase_events;
 } dsa_attn_args;
 
 /* A stack of n_layers DSA layers, each = (indexer + top-k if F) + sparse
  * attention, with one shared index buffer (the IndexCache cache).
  *
  * `indexer` and `attn` give the shapes and dtype shared by all layers; their
- * pointer fields (and workspace fields) are ignored. The per-layer pointers
+ * pointer, workspace and phase_events fields are ignored. The per-layer pointers
  * are HOST arrays of n_layers DEVICE pointers. q_scale / k_scale arrays are
  * required for fp8 and must be NULL for bf16. lse may be NULL (no lse) or an
  * array whose entries may be NULL. out entries may alias each other.

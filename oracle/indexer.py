@@ -48,21 +48,23 @@ def indexer_scores_rows(q_bits, k_bits, w, rows: Sequence[int], *, dtype: str = 
                         batch: int = 0) -> np.ndarray:
     """Scores of the given query rows of one batch entry: [len(rows), n_k] float64,
     -inf where the key is not causal for that row."""
-    Q, K = _dequant(q_bits[batch:batch + 1], k_bits[batch:batch + 1], dtype,
-                    None if q_scale is None else np.asarray(q_scale)[batch:batch + 1],
+    rows = [int(t) for t in rows]
+    # only the requested query rows are dequantised
+    Q, K = _dequant(np.asarray(q_bits)[batch:batch + 1, rows], k_bits[batch:batch + 1], dtype,
+                    None if q_scale is None else np.asarray(q_scale)[batch:batch + 1, rows],
                     None if k_scale is None else np.asarray(k_scale)[batch:batch + 1])
-    Q = Q[0]
+    Q = Q[0]                                   # [len(rows), H, D]
     K = K[0]
     W = np.asarray(w, dtype=np.float64)[batch]
     n_k = K.shape[0]
     out = np.full((len(rows), n_k), -np.inf)
     for r, t in enumerate(rows):
-        p = pos_offset + int(t)
+        p = pos_offset + t
         n = min(p + 1, n_k)
         if n <= 0:
             continue
         # X[j, s] = Q[t,j,:] . K[s,:]  for the causal keys of this row.
-        X = Q[t] @ K[:n].T
+        X = Q[r] @ K[:n].T
         out[r, :n] = W[t] @ np.maximum(X, 0.0)
     if not np.all(np.isfinite(out[out != -np.inf])):
         raise ValueError("non-finite score: inputs must be finite")
