@@ -64,7 +64,7 @@ dsa_status check_indexer_shape(const dsa_indexer_args* a, const char* what) {
     return fail(DSA_ERR_UNSUPPORTED, "%s: topk=%d outside 1..%d", what, a->topk, kMaxTopk);
   int64_t n;
   if (!count4(a->B, a->n_q, a->n_heads, a->head_dim, &n) || !count4(a->B, a->n_q, a->n_k, 1, &n) ||
-      !count4(a->B, a->n_q, dsa::cand_capacity(a->topk), 8, &n))
+      !count4(a->B, a->n_q, dsa::cand_capacity(a->topk, a->n_q == 1), 8, &n))
     return fail(DSA_ERR_INVALID_ARGUMENT, "%s: sizes overflow int64", what);
   return DSA_OK;
 }
@@ -193,7 +193,7 @@ namespace dsa {
 
 size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk) {
   const size_t rows = (size_t)B * n_q;
-  const size_t C = (size_t)cand_capacity(topk);
+  const size_t C = (size_t)cand_capacity(topk, n_q == 1);
   size_t sz = 0;
   sz += round_up(rows * C * 4, 256);  // cand_key
   sz += round_up(rows * C * 4, 256);  // cand_idx
@@ -207,7 +207,7 @@ size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk) {
 
 void indexer_bind_workspace(IndexerParams& p, void* ws) {
   const size_t rows = (size_t)p.B * p.n_q;
-  p.C = cand_capacity(p.topk);
+  p.C = cand_capacity(p.topk, p.n_q == 1);
   char* c = (char*)ws;
   p.cand_key = (uint32_t*)c;
   c += round_up(rows * p.C * 4, 256);

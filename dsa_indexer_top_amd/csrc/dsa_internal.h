@@ -8,10 +8,12 @@
 
 namespace dsa {
 
-// Candidate-list capacity per query row of the streaming top-k: room for the
-// k kept winners plus at least two 64-key tiles of new arrivals.
-inline int cand_capacity(int topk) {
-  int c = topk * 2;
+// Candidate-list capacity per query row. Prefill (streaming filter): room
+// for the kept superset of the top-k plus new arrivals; shrinks cost about
+// C / (C - k) list passes per accepted key, so 4k is used. Decode (one
+// threshold pass): 2k.
+inline int cand_capacity(int topk, bool decode) {
+  int c = topk * (decode ? 2 : 4);
   if (c < topk + 128) c = topk + 128;
   return (c + 63) / 64 * 64;
 }

@@ -59,13 +59,15 @@ __device__ int block_excl_scan(int v, int* scratch /* >= 17 ints */, int* total)
   return r;
 }
 
-// Exact top-k of a full row of n keys (index = position) into s[0..k_eff),
-// unsorted. Used when a decode candidate list overflowed.
-__device__ void block_select_full_row(const uint32_t* __restrict__ keys, int n, int k_eff,
-                                      uint64_t* s, uint32_t* hist /*256*/, int* scratch) {
-  uint32_t prefix = 0u, pmask = 0u;
-  int remaining = k_eff;
+// The k-th largest of keys[0..n) (1 <= k <= n), by 4 radix steps of 8 bits
+// over a 256-bin LDS histogram: *theta = that key, *need = how many keys equal
+// to theta belong to the k largest when ties go to the lowest index.
+// keys may live in LDS or global memory. Called by the whole workgroup.
+__device__ void block_kth_key(const uint32_t* keys, int n, int k, uint32_t* hist, uint32_t* theta,
+                              int* need) {
   __shared__ int sh_digit, sh_above;
+  uint32_t prefix = 0u, pmask = 0u;
+  int remaining = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
     __syncthreads();
@@ -76,7 +78,7 @@ __device__ void block_select_full_row(const uint32_t* __restrict__ keys, int n, 
     __syncthreads();
     if (threadIdx.x < kWave) {
       const int lane = threadIdx.x;
-      const int hb = 255 - 4 * lane;
+      const int hb = 255 - 4 * lane;  // lane order = descending digit order
       const uint32_t c0 = hist[hb], c1 = hist[hb - 1], c2 = hist[hb - 2], c3 = hist[hb - 3];
       const uint32_t loc = c0 + c1 + c2 + c3;
       const uint32_t incl = wave_incl_scan(loc);
@@ -106,22 +108,34 @@ __device__ void block_select_full_row(const uint32_t* __restrict__ keys, int n, 
     remaining -= sh_above;
     __syncthreads();
   }
-  const uint32_t theta = prefix;
-  const int need = remaining;
-  int out = 0, ties = 0;
-  for (int base = 0; base < n; base += blockDim.x) {
-    const int i = base + threadIdx.x;
-    const bool in = i < n;
-    const uint32_t u = in ? keys[i] : 0u;
-    const bool tie = in && u == theta;
-    int tie_total;
-    const int tie_rank = ties + block_excl_scan(tie ? 1 : 0, scratch, &tie_total);
-    const bool keep = in && (u > theta || (tie && tie_rank < need));
-    int keep_total;
-    const int kpos = out + block_excl_scan(keep ? 1 : 0, scratch, &keep_total);
-    if (keep) s[kpos] = composite(u, i);
-    ties += tie_total;
-    out += keep_total;
+  *theta = prefix;
+  *need = remaining;
+}
+
+// Writes, in list order, the composite keys of the entries of keys[0..n) that
+// are > theta plus the first `need` equal to theta, to s[0..). idx[i] is the
+// token index of entry i (NULL: the entry's position). Each thread owns one
+// contiguous segment, so two block-wide scans place every entry.
+__device__ void block_ordered_collect(const uint32_t* keys, const int32_t* __restrict__ idx, int n,
+                                      uint32_t theta, int need, uint64_t* s, int* scratch) {
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int i0 = min((int)threadIdx.x * per, n), i1 = min(i0 + per, n);
+  int ties = 0;
+  for (int i = i0; i < i1; ++i) ties += keys[i] == theta;
+  int tie_total;
+  int tie_rank = block_excl_scan(ties, scratch, &tie_total);
+  int keeps = 0;
+  for (int i = i0, tr = tie_rank; i < i1; ++i) {
+    const uint32_t u = keys[i];
+    if (u > theta) ++keeps;
+    else if (u == theta) keeps += (tr++ < need);
+  }
+  int keep_total;
+  int pos = block_excl_scan(keeps, scratch, &keep_total);
+  for (int i = i0, tr = tie_rank; i < i1; ++i) {
+    const uint32_t u = keys[i];
+    const bool keep = u > theta || (u == theta && tr++ < need);
+    if (keep) s[pos++] = composite(u, idx ? idx[i] : i);
   }
   __syncthreads();
 }
@@ -136,7 +150,58 @@ struct FinalizeParams {
   float* out_scores;
 };
 
-__global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(FinalizeParams p) {
+__device__ void write_sorted(const FinalizeParams& p, int r, const uint64_t* s, int n_sorted) {
+  int32_t* oi = p.out_idx + (size_t)r * p.topk;
+  float* os = p.out_scores ? p.out_scores + (size_t)r * p.topk : nullptr;
+  for (int i = threadIdx.x; i < p.topk; i += blockDim.x) {
+    const bool v = i < n_sorted;
+    const uint64_t c = v ? s[i] : 0ull;
+    oi[i] = v ? (int32_t)(~(uint32_t)c) : -1;
+    if (os) os[i] = v ? key_score((uint32_t)(c >> 32)) : -__builtin_inff();
+  }
+}
+
+__device__ void pad_and_sort(uint64_t* s, int n_items) {
+  int n = 1;
+  while (n < n_items) n <<= 1;
+  for (int i = n_items + threadIdx.x; i < n; i += blockDim.x) s[i] = 0ull;
+  __syncthreads();
+  block_bitonic_desc(s, n);
+}
+
+// Prefill rows: each candidate list (<= kPrefillMaxC entries, in index order)
+// is a superset of the row's top-k. The exact k-th key is found in LDS, the k
+// winners are collected in list order (ties: lowest index) and sorted.
+constexpr int kPrefillMaxC = 8192;
+constexpr int kMaxTopk = 2048;
+
+__global__ __launch_bounds__(kFinNT) void prefill_finalize_kernel(FinalizeParams p) {
+  __shared__ uint32_t skey[kPrefillMaxC];
+  __shared__ uint64_t s[kMaxTopk];
+  __shared__ uint32_t hist[256];
+  __shared__ int scratch[17];
+  const int r = blockIdx.x;
+  const int t = r % p.n_q;
+  const int n_valid = min(p.pos_offset + t + 1, p.n_k);
+  const int k_eff = min(p.topk, n_valid);
+  const int cnt = min(p.cand_cnt[r], p.C);  // >= k_eff by construction
+  const uint32_t* ck = p.cand_key + (size_t)r * p.C;
+  const int32_t* ci = p.cand_idx + (size_t)r * p.C;
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
+  __syncthreads();
+  uint32_t theta = 0u;
+  int need = 1 << 30;
+  const int take = min(k_eff, cnt);
+  if (cnt > take) block_kth_key(skey, cnt, take, hist, &theta, &need);
+  block_ordered_collect(skey, ci, cnt, theta, need, s, scratch);
+  pad_and_sort(s, take);
+  write_sorted(p, r, s, take);
+}
+
+// Decode requests: the candidate list (unordered, <= C = kFinMax entries) is
+// sorted whole; if it overflowed, the exact top-k is taken from the request's
+// full key row instead.
+__global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(FinalizeParams p) {
   __shared__ uint64_t s[kFinMax];
   __shared__ uint32_t hist[256];
   __shared__ int scratch[17];
@@ -149,29 +214,19 @@ __global__ __launch_bounds__(kFinNT) void topk_finalize_kernel(FinalizeParams p)
   if (cnt <= p.C) {
     const uint32_t* ck = p.cand_key + (size_t)r * p.C;
     const int32_t* ci = p.cand_idx + (size_t)r * p.C;
-    int n = 1;
-    while (n < cnt) n <<= 1;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) s[i] = i < cnt ? composite(ck[i], ci[i]) : 0ull;
-    __syncthreads();
-    block_bitonic_desc(s, n);
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) s[i] = composite(ck[i], ci[i]);
+    pad_and_sort(s, cnt);
     n_sorted = min(cnt, k_eff);
   } else {
-    block_select_full_row(p.full_keys + (size_t)r * p.n_k, n_valid, k_eff, s, hist, scratch);
-    int n = 1;
-    while (n < k_eff) n <<= 1;
-    for (int i = k_eff + threadIdx.x; i < n; i += blockDim.x) s[i] = 0ull;
-    __syncthreads();
-    block_bitonic_desc(s, n);
+    const uint32_t* keys = p.full_keys + (size_t)r * p.n_k;
+    uint32_t theta;
+    int need;
+    block_kth_key(keys, n_valid, k_eff, hist, &theta, &need);
+    block_ordered_collect(keys, nullptr, n_valid, theta, need, s, scratch);
+    pad_and_sort(s, k_eff);
     n_sorted = k_eff;
   }
-  int32_t* oi = p.out_idx + (size_t)r * p.topk;
-  float* os = p.out_scores ? p.out_scores + (size_t)r * p.topk : nullptr;
-  for (int i = threadIdx.x; i < p.topk; i += blockDim.x) {
-    const bool v = i < n_sorted;
-    const uint64_t c = v ? s[i] : 0ull;
-    oi[i] = v ? (int32_t)(~(uint32_t)c) : -1;
-    if (os) os[i] = v ? key_score((uint32_t)(c >> 32)) : -__builtin_inff();
-  }
+  write_sorted(p, r, s, n_sorted);
 }
 
 hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s) {
@@ -188,7 +243,10 @@ hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s
   p.full_keys = ip.dec_keys;
   p.out_idx = ip.out_idx;
   p.out_scores = ip.out_scores;
-  hipLaunchKernelGGL(topk_finalize_kernel, dim3(rows), dim3(kFinNT), 0, s, p);
+  if (ip.n_q == 1)
+    hipLaunchKernelGGL(decode_finalize_kernel, dim3(rows), dim3(kFinNT), 0, s, p);
+  else
+    hipLaunchKernelGGL(prefill_finalize_kernel, dim3(rows), dim3(kFinNT), 0, s, p);
   return hipGetLastError();
 }
 
