@@ -14,7 +14,7 @@ namespace dsa {
 // threshold pass): 2k.
 inline int cand_capacity(int topk, bool decode) {
   int c = topk * (decode ? 2 : 4);
-  if (c < topk + 128) c = topk + 128;
+  if (c < topk + 256) c = topk + 256;
   return (c + 63) / 64 * 64;
 }
 

@@ -50,97 +50,150 @@ struct KTile {
   static constexpr int kBytes = kTileKeys * kLdsRow;
 };
 
-// Radix-select step over one 8-bit digit of the keys whose bits above `shift+8`
-// equal `prefix` (under `pmask`): builds the 256-bin histogram in `hist` (LDS
-// of this wave) reading the list 8 keys per lane per batch, then returns the
-// digit d holding the rem-th largest such key and the number of such keys
-// with a digit above d (via *above) and in d (via *in_d).
-__device__ __forceinline__ int wave_digit_step(const uint32_t* __restrict__ keys, int cnt, uint32_t prefix,
-                                               uint32_t pmask, int shift, uint32_t rem, uint32_t* hist,
-                                               uint32_t* above, uint32_t* in_d) {
-  const int lane = lane_id();
-  for (int i = lane; i < 256; i += kWave) hist[i] = 0u;
-  wave_sync();
-  for (int base = 0; base < cnt; base += 8 * kWave) {
-    uint32_t u[8];
+// Workgroup-shared scratch of the cooperative list shrink.
+struct ShrinkLds {
+  uint32_t hist[256];
+  int scan[kPrefillWaves + 1];
+  int res[4];                       // digit, keys above the digit, keys in the digit
+  uint32_t flags[2];                // bit w: the row of wave w needs a shrink (by parity)
+  int cnt[kPrefillWaves];           // that row's list length (in), new length (out)
+  uint32_t theta[kPrefillWaves];    // new acceptance threshold (out)
+};
+
+// Exclusive prefix sum over the workgroup (one value per thread, list order =
+// thread order); *total = sum. Contains barriers: call from every thread.
+__device__ int coop_excl_scan(int v, ShrinkLds& sh, int* total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan((uint32_t)v);
+  if (lane == 63) sh.scan[wave] = (int)incl;
+  __syncthreads();
+  int before = 0, all = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * kWave + lane;
-      u[j] = i < cnt ? keys[i] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * kWave + lane;
-      if (i < cnt && (u[j] & pmask) == prefix) atomicAdd(&hist[(u[j] >> shift) & 255u], 1u);
-    }
+  for (int w = 0; w < kPrefillWaves; ++w) {
+    const int x = sh.scan[w];
+    before += w < wave ? x : 0;
+    all += x;
   }
-  wave_sync();
-  // lane l owns digits 255-4l .. 252-4l, so lane order is descending digit order
-  const int hb = 255 - 4 * lane;
-  const uint32_t c0 = hist[hb], c1 = hist[hb - 1], c2 = hist[hb - 2], c3 = hist[hb - 3];
-  const uint32_t loc = c0 + c1 + c2 + c3;
-  const uint32_t incl = wave_incl_scan(loc);
-  const uint64_t m = ballot(incl >= rem);
-  const int L = uniform_i(m ? __builtin_ctzll(m) : 63);
-  const uint32_t cum = incl - loc;
-  int digit;
-  uint32_t ab, in;
-  if (cum + c0 >= rem) {
-    digit = hb; ab = cum; in = c0;
-  } else if (cum + c0 + c1 >= rem) {
-    digit = hb - 1; ab = cum + c0; in = c1;
-  } else if (cum + c0 + c1 + c2 >= rem) {
-    digit = hb - 2; ab = cum + c0 + c1; in = c2;
-  } else {
-    digit = hb - 3; ab = cum + c0 + c1 + c2; in = c3;
-  }
-  *above = (uint32_t)__builtin_amdgcn_readlane((int)ab, L);
-  *in_d = (uint32_t)__builtin_amdgcn_readlane((int)in, L);
-  wave_sync();
-  return __builtin_amdgcn_readlane(digit, L);
+  __syncthreads();
+  *total = all;
+  return before + (int)incl - v;
 }
 
-// Stable in-place compaction of the first `cnt` entries: keeps every key
-// > theta and the first `ties_left` keys == theta, in list order. Returns the
-// new count.
-__device__ __forceinline__ int wave_compact_keep(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs,
-                                                 int cnt, uint32_t theta, int ties_left) {
-  const int lane = lane_id();
-  int out = 0, ties = 0;
-  for (int base = 0; base < cnt; base += 8 * kWave) {
-    uint32_t u[8];
-    int32_t s[8];
+// One radix-select step over an 8-bit digit of the listed keys whose higher
+// bits match `prefix` under `pmask`: the whole workgroup builds the 256-bin
+// histogram (4 keys in flight per thread), wave 0 finds the digit holding the
+// rem-th largest such key. Returns the digit; *above / *in_d = matching keys
+// with a larger digit / with this digit.
+__device__ int coop_digit_step(const uint32_t* __restrict__ keys, int cnt, uint32_t prefix, uint32_t pmask,
+                               int shift, uint32_t rem, ShrinkLds& sh, uint32_t* above, uint32_t* in_d) {
+  constexpr int NT = kPrefillWaves * kWave;
+  for (int i = threadIdx.x; i < 256; i += NT) sh.hist[i] = 0u;
+  __syncthreads();
+  constexpr int DB = 4;  // keys in flight per thread
+#pragma unroll 1
+  for (int base = 0; base < cnt; base += DB * NT) {
+    uint32_t u[DB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * kWave + lane;
+    for (int j = 0; j < DB; ++j) {
+      const int i = base + j * NT + (int)threadIdx.x;
       u[j] = i < cnt ? keys[i] : 0u;
-      s[j] = i < cnt ? idxs[i] : 0;
     }
-    // every write of this batch lands at or below the chunk being processed,
-    // and the whole batch was read above
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool in = base + j * kWave + lane < cnt;
-      const bool tie = in && u[j] == theta;
-      const uint64_t tm = ballot(tie);
-      const bool keep = in && (u[j] > theta || (tie && ties + mbcnt(tm) < ties_left));
-      ties += popc64(tm);
-      const uint64_t km = ballot(keep);
-      if (keep) {
-        const int o = out + mbcnt(km);
-        keys[o] = u[j];
-        idxs[o] = s[j];
-      }
-      out += popc64(km);
+    for (int j = 0; j < DB; ++j) {
+      const int i = base + j * NT + (int)threadIdx.x;
+      if (i < cnt && (u[j] & pmask) == prefix) atomicAdd(&sh.hist[(u[j] >> shift) & 255u], 1u);
     }
   }
-  wave_sync();
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int hb = 255 - 4 * lane;  // lane order = descending digit order
+    const uint32_t c0 = sh.hist[hb], c1 = sh.hist[hb - 1], c2 = sh.hist[hb - 2], c3 = sh.hist[hb - 3];
+    const uint32_t loc = c0 + c1 + c2 + c3;
+    const uint32_t incl = wave_incl_scan(loc);
+    const uint64_t m = ballot(incl >= rem);
+    const int L = uniform_i(m ? __builtin_ctzll(m) : 63);
+    const uint32_t cum = incl - loc;
+    int digit;
+    uint32_t ab, in;
+    if (cum + c0 >= rem) {
+      digit = hb; ab = cum; in = c0;
+    } else if (cum + c0 + c1 >= rem) {
+      digit = hb - 1; ab = cum + c0; in = c1;
+    } else if (cum + c0 + c1 + c2 >= rem) {
+      digit = hb - 2; ab = cum + c0 + c1; in = c2;
+    } else {
+      digit = hb - 3; ab = cum + c0 + c1 + c2; in = c3;
+    }
+    if (lane == L) {
+      sh.res[0] = digit;
+      sh.res[1] = (int)ab;
+      sh.res[2] = (int)in;
+    }
+  }
+  __syncthreads();
+  *above = (uint32_t)sh.res[1];
+  *in_d = (uint32_t)sh.res[2];
+  const int d = sh.res[0];
+  __syncthreads();
+  return d;
+}
+
+// Ordered in-place compaction by the workgroup: keeps every key > theta and
+// the first `ties_left` keys == theta, in list order; returns the new length.
+// Each thread owns CE consecutive entries of a round; all of a round is read
+// before any of it is written (the scans hold barriers), and a round only
+// writes below its own end.
+__device__ int coop_compact(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, int cnt, uint32_t theta,
+                            int ties_left, ShrinkLds& sh) {
+  constexpr int NT = kPrefillWaves * kWave;
+  constexpr int CE = 4;
+  int out = 0, ties = 0;
+#pragma unroll 1
+  for (int base = 0; base < cnt; base += CE * NT) {
+    const int i0 = base + CE * (int)threadIdx.x;
+    uint32_t u[CE];
+    int32_t s[CE];
+    int nt = 0;
+#pragma unroll
+    for (int j = 0; j < CE; ++j) {
+      const bool in = i0 + j < cnt;
+      u[j] = in ? keys[i0 + j] : 0u;
+      s[j] = in ? idxs[i0 + j] : 0;
+      nt += (in && u[j] == theta) ? 1 : 0;
+    }
+    int tie_total;
+    int tr = ties + coop_excl_scan(nt, sh, &tie_total);
+    int nk = 0;
+    uint32_t keep = 0u;
+#pragma unroll
+    for (int j = 0; j < CE; ++j) {
+      const bool in = i0 + j < cnt;
+      const bool kj = in && (u[j] > theta || (u[j] == theta && tr++ < ties_left));
+      keep |= kj ? (1u << j) : 0u;
+      nk += kj ? 1 : 0;
+    }
+    int keep_total;
+    int pos = out + coop_excl_scan(nk, sh, &keep_total);
+#pragma unroll
+    for (int j = 0; j < CE; ++j) {
+      if ((keep >> j) & 1u) {
+        keys[pos] = u[j];
+        idxs[pos] = s[j];
+        ++pos;
+      }
+    }
+    out += keep_total;
+    ties += tie_total;
+    __syncthreads();
+  }
   return out;
 }
 
 // Shrinks one row's candidate list (cnt > k entries, all of keys earlier than
-// any future arrival) so that it still holds the row's top-k, and returns the
-// new acceptance threshold: a later key is kept iff its key is > threshold.
+// any future arrival) so that it still holds the row's top-k; run by the whole
+// workgroup. Returns the new acceptance threshold (a later key is kept iff
+// its key is > threshold) and the new length.
 // Fast path: two 8-bit digit steps find the 16-bit prefix P of the k-th largest
 // key; at least k listed keys are >= theta = P<<16, so a later key <= theta
 // ranks below k earlier ones (ties go to the lower index) and can be dropped,
@@ -148,31 +201,27 @@ __device__ __forceinline__ int wave_compact_keep(uint32_t* __restrict__ keys, in
 // If that keeps too many (heavy ties), two more digit steps give the exact
 // k-th key theta and the list keeps exactly k entries: those > theta and the
 // lowest-index ties (the list is in index order).
-__device__ __noinline__ uint32_t wave_shrink(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs,
-                                             int* cnt_io, int k, int keep_max, uint32_t* hist) {
-  const int cnt = *cnt_io;
-  wave_sync();
-  uint32_t above, in_d;
+__device__ __forceinline__ void coop_shrink(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, int cnt, int k,
+                                            int keep_max, ShrinkLds& sh, uint32_t* theta_out, int* cnt_out) {
+  uint32_t prefix = 0u, pmask = 0u;
   uint32_t rem = (uint32_t)k;
-  const int d1 = wave_digit_step(keys, cnt, 0u, 0u, 24, rem, hist, &above, &in_d);
-  rem -= above;
-  uint32_t prefix = (uint32_t)d1 << 24;
-  const int d2 = wave_digit_step(keys, cnt, prefix, 0xFF000000u, 16, rem, hist, &above, &in_d);
-  rem -= above;
-  prefix |= (uint32_t)d2 << 16;
-  const uint32_t kept = (uint32_t)k - rem + in_d;  // keys with prefix >= P
-  if ((int)kept <= keep_max) {
-    *cnt_io = wave_compact_keep(keys, idxs, cnt, prefix, 1 << 30);
-    return prefix;
+  int ties_left = 1 << 30;
+#pragma unroll 1
+  for (int st = 0; st < 4; ++st) {
+    uint32_t above, in_d;
+    const int shift = 24 - 8 * st;
+    const int d = coop_digit_step(keys, cnt, prefix, pmask, shift, rem, sh, &above, &in_d);
+    rem -= above;
+    prefix |= (uint32_t)d << shift;
+    pmask |= 0xFFu << shift;
+    if (st == 1 && (int)((uint32_t)k - rem + in_d) <= keep_max) break;  // keys with prefix >= P fit
+    if (st == 3) ties_left = (int)rem;
   }
-  const int d3 = wave_digit_step(keys, cnt, prefix, 0xFFFF0000u, 8, rem, hist, &above, &in_d);
-  rem -= above;
-  prefix |= (uint32_t)d3 << 8;
-  const int d4 = wave_digit_step(keys, cnt, prefix, 0xFFFFFF00u, 0, rem, hist, &above, &in_d);
-  rem -= above;
-  prefix |= (uint32_t)d4;
-  *cnt_io = wave_compact_keep(keys, idxs, cnt, prefix, (int)rem);
-  return prefix;
+  const int n = coop_compact(keys, idxs, cnt, prefix, ties_left, sh);
+  if (threadIdx.x == 0) {
+    *theta_out = prefix;
+    *cnt_out = n;
+  }
 }
 
 template <int D, int MB, bool FP8, bool DUMP>
@@ -182,10 +231,10 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void indexer_prefill_kernel(
   constexpr int KS = FP8 ? D / 64 : D / 16;  // MFMA k-steps over head_dim
   constexpr int CPT = (T::kChunks + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][T::kBytes];
-  __shared__ uint32_t lds_hist[kPrefillWaves][256];
+  __shared__ ShrinkLds shl;
 
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform_i(threadIdx.x >> 6);  // wave-uniform: row state lives in SGPRs
   const int nqb = (p.n_q + kPrefillWaves - 1) / kPrefillWaves;
   const int qb = nqb - 1 - (int)blockIdx.x;  // longest rows first
   const int b = blockIdx.y;
@@ -240,30 +289,34 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void indexer_prefill_kernel(
   // Two register stages: the fetch of tile t+2 is issued right after the
   // barrier that publishes tile t+1 and only stored to LDS one full iteration
   // later, so L2/MALL latency hides behind a whole tile of MFMA work.
-  i32x4 stage0[CPT], stage1[CPT];
+  // bf16 with 64 heads and head_dim 128 keeps 64 VGPRs of A fragments; it
+  // uses one stage (fetch issued half an iteration ahead) to stay spill-free.
+  constexpr int NSTAGE = (!FP8 && D == 128 && MB == 2) ? 1 : 2;
+  i32x4 stage0[CPT], stage1[NSTAGE == 2 ? CPT : 1];
   const unsigned char* kbase = (const unsigned char*)p.k + (size_t)b * p.n_k * T::kRowBytes;
-  int ld_row[CPT], ld_goff[CPT], ld_soff[CPT];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
+  // chunk c of this thread: row ch / kChunksPerRow, column ch % kChunksPerRow
+  // (recomputed per use: cheaper than keeping 3 * CPT registers alive)
+  auto ld_row = [&](int c) {
     const int ch = threadIdx.x + c * NT;
-    const int r = ch / T::kChunksPerRow, col = ch % T::kChunksPerRow;
-    ld_row[c] = ch < T::kChunks ? r : (1 << 30);
-    ld_goff[c] = r * T::kRowBytes + col * 16;
-    ld_soff[c] = r * T::kLdsRow + col * 16;
-  }
-  auto load_tile = [&](i32x4 (&st)[CPT], int tile) {
+    return ch < T::kChunks ? ch / T::kChunksPerRow : (1 << 30);
+  };
+  auto ld_col = [&](int c) { return (int)(threadIdx.x + c * NT) % T::kChunksPerRow; };
+  auto load_tile = [&](auto& st, int tile) {
     const unsigned char* src = kbase + (size_t)tile * kTileKeys * T::kRowBytes;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       i32x4 v = {0, 0, 0, 0};
-      if (tile * kTileKeys + ld_row[c] < p.n_k) v = *(const i32x4*)(src + ld_goff[c]);
+      const int r = ld_row(c);
+      if (tile * kTileKeys + r < p.n_k) v = *(const i32x4*)(src + r * T::kRowBytes + ld_col(c) * 16);
       st[c] = v;
     }
   };
-  auto store_tile = [&](const i32x4 (&st)[CPT], int buf) {
+  auto store_tile = [&](const auto& st, int buf) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (ld_row[c] < kTileKeys) *(i32x4*)(&lds_k[buf][ld_soff[c]]) = st[c];
+    for (int c = 0; c < CPT; ++c) {
+      const int r = ld_row(c);
+      if (r < kTileKeys) *(i32x4*)(&lds_k[buf][r * T::kLdsRow + ld_col(c) * 16]) = st[c];
+    }
   };
 
   uint32_t theta = 0u;
@@ -292,8 +345,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void indexer_prefill_kernel(
       return *(const bf16x8*)(src0 + g * D + 16 * ks);
     }
   };
+  constexpr int SIDE_KS = KS > 1 ? 1 : 0;  // chunk that also carries the previous tile's filter
   auto half_step = [&](auto EPI_T, auto MMA_T, const unsigned char* kt, int nb, f32x16 (&acc)[MB],
-                       const f32x16 (&prev)[MB]) -> float {
+                       const f32x16 (&prev)[MB], auto&& side) -> float {
     constexpr bool EPI = decltype(EPI_T)::value;
     constexpr bool MMA = decltype(MMA_T)::value;
     const unsigned char* src0 = kt + (32 * nb + i32) * T::kLdsRow;
@@ -328,80 +382,164 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void indexer_prefill_kernel(
         // otherwise sink it below every fence)
         asm volatile("" : "+v"(s0), "+v"(s1));
       }
+      if (ks == SIDE_KS) side();
       __builtin_amdgcn_sched_barrier(0);
     }
     return s0 + s1;
   };
   using TrueT = std::integral_constant<bool, true>;
   using FalseT = std::integral_constant<bool, false>;
-  // Join the two half-tile partials (v_permlane32_swap: lane l < 32 gets key l
-  // of half 0, lane l >= 32 key l of half 1), then the streaming filter.
-  auto finish_tile = [&](int base, float part0, float part1, float ksc) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part0), __float_as_uint(part1),
+  // Streaming filter of one finished tile, split in two. filter_compute runs
+  // inside a chunk of the next half tile, so its dependency chain (join the
+  // two half-tile partials with v_permlane32_swap: lane l < 32 gets key l of
+  // half 0, lane l >= 32 key l of half 1; order key; compare; ballot) hides
+  // behind MFMAs. filter_commit (after that half tile) takes the rare branch:
+  // append the accepted keys and, when the list is nearly full, shrink it.
+  // A tile is pending from the end of its second half until the next commit;
+  // with nothing pending, pend_end = 0 makes every lane invalid.
+  float pend_p0 = 0.0f, pend_p1 = 0.0f, pend_ksc = 1.0f;
+  int pend_base = 0, pend_end = 0;
+  float f_score = 0.0f;
+  // theta as a float: the order key is strictly monotone on scores, so
+  // key > theta  <=>  score > key_score(theta) (and -inf accepts all).
+  float theta_f = -__builtin_inff();
+  auto filter_compute = [&]() {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pend_p0), __float_as_uint(pend_p1),
                                                      false, false);
     float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int key = base + lane;
-    const bool valid = key < kend;
-    if constexpr (FP8) score *= ksc;
+    if constexpr (FP8) score *= pend_ksc;
+    f_score = score;
+    asm volatile("" : "+v"(f_score));
+  };
+  // par: parity of the iteration; a full list raises flag bit `wave` of
+  // flags[par], which the workgroup serves after the next barrier.
+  auto filter_commit = [&](int par) {
+    const int key = pend_base + lane;
+    const bool valid = key < pend_end;
     if constexpr (DUMP) {
-      if (valid) p.dump[row * (size_t)p.n_k + key] = canon_zero(score);
+      if (valid) p.dump[row * (size_t)p.n_k + key] = canon_zero(f_score);
     }
-    const uint32_t u = score_key(score);
-    const bool accept = valid && u > theta;
-    const uint64_t am = ballot(accept);
+    const uint64_t am = ballot(valid && f_score > theta_f);
     if (am) {
-      if (accept) {
+      if ((am >> lane) & 1ull) {
         const int pos = cnt + mbcnt(am);
-        ckey[pos] = u;
+        ckey[pos] = score_key(f_score);
         cidx[pos] = key;
       }
       cnt += popc64(am);
-      if (cnt > p.C - kTileKeys) {
-        theta = uniform_u(wave_shrink(ckey, cidx, &cnt, p.topk, p.C - 2 * kTileKeys, lds_hist[wave]));
-        cnt = uniform_i(cnt);
-      }
+      if (cnt > p.C - 3 * kTileKeys && lane == 0) atomicOr(&shl.flags[par], 1u << wave);
     }
+    pend_end = 0;
   };
+  // Called by the whole workgroup with the flags word it read after the
+  // barrier: shrinks every flagged row, one at a time; each flagged wave picks
+  // up its new threshold and length; the word is cleared for its next use.
+  auto coop_shrinks = [&](uint32_t flags, int par) {
+    if (flags == 0u) return;
+    if (lane == 0) shl.cnt[wave] = cnt;  // current lengths (a commit may have followed the flag)
+    __syncthreads();
+#pragma unroll 1
+    for (int w = 0; w < kPrefillWaves; ++w) {
+      if (!((flags >> w) & 1u) || shl.cnt[w] <= p.C - 3 * kTileKeys) continue;
+      const size_t rw = (size_t)b * p.n_q + qb * kPrefillWaves + w;
+      coop_shrink(p.cand_key + rw * p.C, p.cand_idx + rw * p.C, shl.cnt[w], p.topk, p.C - 3 * kTileKeys, shl,
+                  &shl.theta[w], &shl.cnt[w]);
+      __syncthreads();
+    }
+    if (((flags >> wave) & 1u) && cnt > p.C - 3 * kTileKeys) {
+      theta = uniform_u(shl.theta[wave]);
+      theta_f = key_score(theta);
+      cnt = uniform_i(shl.cnt[wave]);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) shl.flags[par] = 0u;
+    __syncthreads();
+  };
+  auto no_side = [&]() {};
 
   f32x16 accA[MB], accB[MB];
   if (n_tiles > 0) {
     load_tile(stage0, 0);
     store_tile(stage0, 0);
   }
-  if (n_tiles > 1) load_tile(stage1, 1);
+  if constexpr (NSTAGE == 2) {
+    if (n_tiles > 1) load_tile(stage1, 1);
+  }
+  if (threadIdx.x == 0) {
+    shl.flags[0] = 0u;
+    shl.flags[1] = 0u;
+  }
   // Nothing may stay in flight into the loop: the loop's own prefetches are
   // then the only outstanding loads the MFMAs could be made to wait for.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (kend > 0) half_step(FalseT{}, TrueT{}, lds_k[0], 0, accA, accB);
-  // One tile: second half-tile of `tile` (+ epilogue of its first half), then
-  // publish tile+1 (held in st_next) and start fetching tile+2 into st_free,
-  // then the first half of tile+1 (+ epilogue of tile's second half).
-  auto iteration = [&](int tile, const i32x4 (&st_next)[CPT], i32x4 (&st_free)[CPT]) {
+  if (kend > 0) half_step(FalseT{}, TrueT{}, lds_k[0], 0, accA, accB, no_side);
+  // One tile: second half-tile of `tile` (+ epilogue of its first half, + the
+  // previous tile's filter), then publish tile+1 (held in st_next) and start
+  // fetching tile+2 into st_free, then the first half of tile+1 (+ epilogue of
+  // tile's second half); `tile` is then pending for the filter.
+  auto iteration = [&](int tile, auto& st_next, auto& st_free) {
     const int cur = tile & 1;
     const bool more = tile + 1 < n_tiles;
+    if constexpr (NSTAGE == 1) {
+      if (more) load_tile(stage0, tile + 1);
+    }
     const int base = tile * kTileKeys;
     const bool mine = base < kend;                          // wave-uniform
     const bool mine_next = more && base + kTileKeys < kend;
     float ksc = 1.0f;
     if constexpr (FP8) ksc = (mine && base + lane < kend) ? kscale[base + lane] : 0.0f;
     float part0 = 0.0f, part1 = 0.0f;
-    if (mine) part0 = half_step(TrueT{}, TrueT{}, lds_k[cur], 1, accB, accA);
-    if (more) store_tile(st_next, cur ^ 1);
+    const int par = tile & 1;
+    if (mine) part0 = half_step(TrueT{}, TrueT{}, lds_k[cur], 1, accB, accA, filter_compute);
+    else filter_compute();
+    if constexpr (NSTAGE == 1) {
+      if (more) store_tile(stage0, cur ^ 1);
+    } else {
+      if (more) store_tile(st_next, cur ^ 1);
+    }
     __syncthreads();
-    if (tile + 2 < n_tiles) load_tile(st_free, tile + 2);
+    // Appends go out right after the barrier: the next wait on the vector
+    // memory counter (for the next K tile) is then half a tile away, so the
+    // stores' acknowledgements are not waited for on the spot.
+    filter_commit(par);
+    // The flags raised by the previous iteration's commits (other parity) are
+    // visible now; read them during the next half tile and serve them after
+    // it (the word is next written two iterations later, after a barrier).
+    uint32_t flags_v = 0u;
+    auto read_flags = [&]() { flags_v = shl.flags[par ^ 1]; };
+    if constexpr (NSTAGE == 2) {
+      if (tile + 2 < n_tiles) load_tile(st_free, tile + 2);
+    }
     if (mine) {
       if (mine_next)
-        part1 = half_step(TrueT{}, TrueT{}, lds_k[cur ^ 1], 0, accA, accB);
+        part1 = half_step(TrueT{}, TrueT{}, lds_k[cur ^ 1], 0, accA, accB, read_flags);
       else
-        part1 = half_step(TrueT{}, FalseT{}, lds_k[cur], 0, accA, accB);
-      finish_tile(base, part0, part1, ksc);
+        part1 = half_step(TrueT{}, FalseT{}, lds_k[cur], 0, accA, accB, read_flags);
+      pend_p0 = part0;
+      pend_p1 = part1;
+      pend_ksc = ksc;
+      pend_base = base;
+      pend_end = kend;
+    } else {
+      read_flags();
     }
+    coop_shrinks(uniform_u(flags_v), par ^ 1);
   };
-  for (int tile = 0; tile < n_tiles; tile += 2) {
-    iteration(tile, stage1, stage0);
-    if (tile + 1 < n_tiles) iteration(tile + 1, stage0, stage1);
+  if constexpr (NSTAGE == 2) {
+    for (int tile = 0; tile < n_tiles; tile += 2) {
+      iteration(tile, stage1, stage0);
+      if (tile + 1 < n_tiles) iteration(tile + 1, stage0, stage1);
+    }
+  } else {
+    for (int tile = 0; tile < n_tiles; ++tile) iteration(tile, stage0, stage0);
   }
+  filter_compute();
+  __syncthreads();
+  filter_commit(n_tiles & 1);
+  __syncthreads();
+  coop_shrinks(uniform_u(shl.flags[(n_tiles & 1) ^ 1]), (n_tiles & 1) ^ 1);
+  coop_shrinks(uniform_u(shl.flags[n_tiles & 1]), n_tiles & 1);
   if (active && lane == 0) p.cand_cnt[row] = cnt;
 }
 
