@@ -51,8 +51,10 @@ struct KTile {
 };
 
 // Workgroup-shared scratch of the cooperative list shrink.
+constexpr int kShrinkHistCopies = 8;  // interleaved copies: clustered keys would serialise one copy
+
 struct ShrinkLds {
-  uint32_t hist[256];
+  uint32_t hist[256 * kShrinkHistCopies];
   int scan[kPrefillWaves + 1];
   int res[4];                       // digit, keys above the digit, keys in the digit
   uint32_t flags[2];                // bit w: the row of wave w needs a shrink (by parity)
@@ -87,8 +89,9 @@ __device__ int coop_excl_scan(int v, ShrinkLds& sh, int* total) {
 __device__ int coop_digit_step(const uint32_t* __restrict__ keys, int cnt, uint32_t prefix, uint32_t pmask,
                                int shift, uint32_t rem, ShrinkLds& sh, uint32_t* above, uint32_t* in_d) {
   constexpr int NT = kPrefillWaves * kWave;
-  for (int i = threadIdx.x; i < 256; i += NT) sh.hist[i] = 0u;
+  for (int i = threadIdx.x; i < 256 * kShrinkHistCopies; i += NT) sh.hist[i] = 0u;
   __syncthreads();
+  const uint32_t copy = threadIdx.x % kShrinkHistCopies;
   constexpr int DB = 4;  // keys in flight per thread
 #pragma unroll 1
   for (int base = 0; base < cnt; base += DB * NT) {
@@ -101,14 +104,22 @@ __device__ int coop_digit_step(const uint32_t* __restrict__ keys, int cnt, uint3
 #pragma unroll
     for (int j = 0; j < DB; ++j) {
       const int i = base + j * NT + (int)threadIdx.x;
-      if (i < cnt && (u[j] & pmask) == prefix) atomicAdd(&sh.hist[(u[j] >> shift) & 255u], 1u);
+      if (i < cnt && (u[j] & pmask) == prefix)
+        atomicAdd(&sh.hist[((u[j] >> shift) & 255u) * kShrinkHistCopies + copy], 1u);
     }
   }
   __syncthreads();
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     const int hb = 255 - 4 * lane;  // lane order = descending digit order
-    const uint32_t c0 = sh.hist[hb], c1 = sh.hist[hb - 1], c2 = sh.hist[hb - 2], c3 = sh.hist[hb - 3];
+    uint32_t c0 = 0u, c1 = 0u, c2 = 0u, c3 = 0u;
+#pragma unroll
+    for (int j = 0; j < kShrinkHistCopies; ++j) {
+      c0 += sh.hist[hb * kShrinkHistCopies + j];
+      c1 += sh.hist[(hb - 1) * kShrinkHistCopies + j];
+      c2 += sh.hist[(hb - 2) * kShrinkHistCopies + j];
+      c3 += sh.hist[(hb - 3) * kShrinkHistCopies + j];
+    }
     const uint32_t loc = c0 + c1 + c2 + c3;
     const uint32_t incl = wave_incl_scan(loc);
     const uint64_t m = ballot(incl >= rem);
