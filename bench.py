@@ -227,6 +227,9 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline + CPU baseline only")
     ap.add_argument("--stack-L", type=int, default=61440)
     ap.add_argument("--stack-layers", type=int, default=47)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 3 times (reference dispatch for "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -241,6 +244,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        assert torch.equal(dst, src)
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
     L, H, D, topk = args.L, 64, 128, 2048
 
     log(f"generating the L={L} {args.dtype} layer")
