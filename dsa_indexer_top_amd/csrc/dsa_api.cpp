@@ -224,11 +224,13 @@ void indexer_bind_workspace(IndexerParams& p, void* ws) {
 
 int attn_nsplit(int B, int n_q, int topk) {
   if (n_q > 1) return 1;
-  // decode: spread one request's gather over many waves (>= 64 entries each)
-  int ns = topk / 64;
-  if (ns < 1) ns = 1;
+  // decode: spread the requests' gathers over about 1024 waves, at least one
+  // 32-entry chunk per split and at most 64 splits (the merge uses one lane each)
+  const int chunks = (topk + 31) / 32;
+  int ns = 1024 / (B > 0 ? B : 1);
+  if (ns > chunks) ns = chunks;
   if (ns > 64) ns = 64;
-  (void)B;
+  if (ns < 1) ns = 1;
   return ns;
 }
 
@@ -236,7 +238,7 @@ size_t attn_workspace_bytes(int B, int n_q, int n_k, int H, int D, int topk) {
   (void)n_k;
   const int ns = attn_nsplit(B, n_q, topk);
   if (ns <= 1) return 0;
-  return round_up((size_t)B * n_q * ns * H * (D + 2) * 4, 256);
+  return round_up((size_t)B * n_q * ns * H * attn_part_stride(D) * 4, 256);
 }
 
 }  // namespace dsa

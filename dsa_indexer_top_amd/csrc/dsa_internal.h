@@ -59,9 +59,15 @@ struct AttnParams {
   void* out;
   float* lse;
   int nsplit;           // >1: split-K over the idx list (decode), partials in ws
-  float* part;          // [rows, nsplit, H, D + 2]
+  float* part;          // [rows, nsplit, H, kAttnPartStride]: O[D], max, sum, pad
   void* const* ev;      // optional phase events (2): before, after
 };
+
+// floats per (query, split, head) partial of split attention: O[D], max, sum,
+// padded so every partial starts 16-byte aligned
+template <int D>
+constexpr int kAttnPartStride = D + 4;
+inline int attn_part_stride(int D) { return D + 4; }
 
 size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk);
 size_t attn_workspace_bytes(int B, int n_q, int n_k, int H, int D, int topk);

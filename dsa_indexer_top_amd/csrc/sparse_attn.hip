@@ -5,16 +5,27 @@
 // heads, so each selected K/V row is gathered once per query and reused by
 // every head.
 //
-// Mapping (gfx950, wave64): one wave per (query, split). The query's heads
-// (padded to 16) are the M dimension of v_mfma_f32_16x16x32_bf16; each chunk
-// of 32 selected keys gives two 16-key N blocks whose K rows are gathered
-// straight from memory into B-fragments (a lane reads 16 contiguous bytes of
-// one row per k-step). Online softmax runs in fp32 with exp2 (scale folded
-// with log2 e). The P.V product runs on the VALU: each lane owns two
-// contiguous output dims for every head, the wave gathers one V row per
-// instruction (fully coalesced), and P is handed over through 2 KB of LDS
-// per wave. Decode (one query per request) splits the index list over many
-// waves and merges the partial (max, sum, O) triples in a second kernel.
+// Mapping (gfx950, wave64): one wave per (query, split); the wave walks its
+// slice of the index list in chunks of 32 entries. Both products run on
+// v_mfma_f32_16x16x32_bf16 with the query's heads (padded to 16) as the
+// 16-wide N dimension:
+//   S^T[key, head] = K_sel . Q^T   A = gathered K rows (a lane reads 16
+//                                  contiguous bytes of one row per k-step),
+//                                  B = Q^T (kept in registers);
+//   O^T[dim, head] += V_sel^T . P^T
+// The S^T accumulator leaves every lane with one head and 8 keys, which is
+// exactly the B operand P^T of the second product (its k-slots are those 8
+// keys), so the probabilities never leave registers and each lane's softmax
+// state (running max, partial sum) is one scalar for its head. The A operand
+// V^T needs 8 keys of one dim per lane: the chunk's 32 V rows are gathered
+// with 16-byte coalesced loads, keys j and j + 16 are interleaved per dim
+// with v_perm (one dword = that dim of both keys) and staged in LDS as 16
+// "pair rows", so each A-operand dword is a single 32-bit LDS read (rows
+// padded so the four lane groups of a read hit disjoint banks). Online
+// softmax in fp32 with exp2 (scale folded with log2 e); P is rounded to bf16
+// for the second product.
+// Decode (one query per request) splits the list over many waves; a second
+// kernel merges the per-split (O, max, sum) triples by the log-sum-exp rule.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -23,194 +34,246 @@ namespace dsa {
 constexpr int kAttnWaves = 4;
 constexpr int kAttnChunk = 32;
 
+template <int D>
+struct AttnShape {
+  static constexpr int KS = D / 32;           // k-steps of S^T over head_dim
+  static constexpr int DB = D / 16;           // 16-dim blocks of O^T
+  static constexpr int LPR = D / 8;           // lanes per V row (16 B each)
+  static constexpr int RPI = kWave / LPR;     // V rows per load instruction
+  static constexpr int VL = kAttnChunk / RPI; // V load instructions per chunk
+  static constexpr int PSTRIDE = 4 * D + 64;  // LDS bytes per pair row (D dwords + pad)
+};
+
+// LDS pair row of the key pair (j, j + 16), j < 16: pair 4g + w sits in row
+// 4w + g, so the four lane groups of a read (pairs 4 apart) touch consecutive
+// rows, which a stride of 4D + 64 bytes places 16 banks apart.
+__device__ __forceinline__ int prow(int j) { return (j & 3) * 4 + (j >> 2); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(kAttnWaves * kWave) void sparse_attn_kernel(AttnParams p) {
-  constexpr int KS = D / 32;       // 16x16x32 k-steps over head_dim
-  constexpr int RG = 128 / D;      // V rows per gather instruction (D=128: 1, D=64: 2)
-  constexpr int DPL = 2;           // output dims per lane
-  __shared__ __attribute__((aligned(16))) float lds_p[kAttnWaves][kAttnChunk][16];
+  using S = AttnShape<D>;
+  static_assert((S::PSTRIDE / 4) % 64 == 16, "lane groups of a read must not share banks");
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v[kAttnWaves][16 * S::PSTRIDE];
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
+  const int ns = p.nsplit;
   const int rows = p.B * p.n_q;
-  const int row = blockIdx.x * kAttnWaves + wave;
-  if (row >= rows) return;  // no workgroup barriers below
+  const int wid = blockIdx.x * kAttnWaves + wave;
+  if (wid >= rows * ns) return;  // no workgroup barriers below
+  const int row = wid / ns;
+  const int split = wid - row * ns;
   const int b = row / p.n_q;
   const int t = row - b * p.n_q;
   const int pos = p.pos_offset + t;
-  const int split = blockIdx.y;
-  const int per = ((p.topk + p.nsplit - 1) / p.nsplit + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
+  const int per = ((p.topk + ns - 1) / ns + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
   const int e0 = split * per;
   const int e1 = min(e0 + per, p.topk);
   const int i16 = lane & 15, g = lane >> 4;
   const float sl2 = p.scale * 1.4426950408889634f;
 
-  // Q fragments: head i16, dims g*(D/4) + 8*ks .. +7
-  bf16x8 qa[KS];
+  // Q^T as the B operand: column = head i16, k-slots = dims g*(D/4) + 8*ks .. +7
+  bf16x8 qb[S::KS];
   {
     const __bf16* qrow = (const __bf16*)p.q + ((size_t)row * p.H + i16) * D + g * (D / 4);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < S::KS; ++ks) {
       bf16x8 v = {};
       if (i16 < p.H) v = *(const bf16x8*)(qrow + 8 * ks);
-      qa[ks] = v;
+      qb[ks] = v;
     }
   }
-  const __bf16* kb = (const __bf16*)p.k + (size_t)b * p.n_k * D;
-  const __bf16* vb = (const __bf16*)p.v + (size_t)b * p.n_k * D;
+  const unsigned char* kb = (const unsigned char*)p.k + (size_t)b * p.n_k * D * 2;
+  const unsigned char* vb = (const unsigned char*)p.v + (size_t)b * p.n_k * D * 2;
   const int32_t* irow = p.idx + (size_t)row * p.topk;
-  const int rg = (RG == 1) ? 0 : (lane >> 5);
-  const int d0 = DPL * (RG == 1 ? lane : (lane & 31));
+  unsigned char* vl = lds_v[wave];
+  const int vr = lane / S::LPR, vc = lane % S::LPR;  // V load: row in group, 16-byte column
 
-  float o[16][DPL];
+  f32x4 o[S::DB];
 #pragma unroll
-  for (int h = 0; h < 16; ++h)
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) o[h][c] = 0.0f;
-  float m[4], l[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -__builtin_inff();
-    l[r] = 0.0f;
-  }
-  float (*P)[16] = lds_p[wave];
+  for (int db = 0; db < S::DB; ++db) o[db] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -__builtin_inff(), l = 0.0f;
 
+  int raw_next = (e0 + (lane & 31) < e1) ? irow[e0 + (lane & 31)] : -1;
   for (int c0 = e0; c0 < e1; c0 += kAttnChunk) {
-    const int e = c0 + (lane & 31);
-    const int raw = e < e1 ? irow[e] : -1;
+    const int raw = raw_next;
+    {
+      const int e = c0 + kAttnChunk + (lane & 31);
+      raw_next = e < e1 ? irow[e] : -1;
+    }
     const bool valid = raw >= 0 && raw <= pos && raw < p.n_k;
     const int key = valid ? raw : 0;
-    float sv[2][4];
+    const uint32_t vmask = (uint32_t)ballot(valid);  // bit j: entry c0 + j is valid
+
+    // gathers: K rows as A fragments, V rows into registers
+    bf16x8 kf[2][S::KS];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int kj = __shfl(key, 16 * nb + i16, 64);
-      const int vj = __shfl(valid ? 1 : 0, 16 * nb + i16, 64);
-      const __bf16* krow = kb + (size_t)kj * D + g * (D / 4);
-      f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+      const unsigned char* krow = kb + (size_t)kj * (D * 2) + g * (D / 2);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(krow + 8 * ks);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kf, s, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[nb][r] = vj ? s[r] * sl2 : -__builtin_inff();
+      for (int ks = 0; ks < S::KS; ++ks) kf[nb][ks] = *(const bf16x8*)(krow + 16 * ks);
     }
-    // online softmax; lane holds heads 4g + r of key 16*nb + i16
-    float corr[4];
+    i32x4 vv[S::VL];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mx = wave_max16(fmaxf(sv[0][r], sv[1][r]));
-      const float mn = fmaxf(m[r], mx);
-      const bool none = mn == -__builtin_inff();
-      corr[r] = none ? 1.0f : exp2f(m[r] - mn);
-      const float p0 = none ? 0.0f : exp2f(sv[0][r] - mn);
-      const float p1 = none ? 0.0f : exp2f(sv[1][r] - mn);
-      l[r] = l[r] * corr[r] + p0 + p1;
-      m[r] = mn;
-      P[i16][4 * g + r] = p0;
-      P[16 + i16][4 * g + r] = p1;
+    for (int i = 0; i < S::VL; ++i) {
+      const int vj = __shfl(key, S::RPI * i + vr, 64);
+      vv[i] = *(const i32x4*)(vb + (size_t)vj * (D * 2) + 16 * vc);
     }
+
+    // S^T = K . Q^T: lane holds head i16, keys 16*nb + 4*g + r
+    f32x4 s[2];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      const float ch = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr[h & 3]), 16 * (h >> 2)));
+    for (int nb = 0; nb < 2; ++nb) {
+      s[nb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) o[h][c] *= ch;
+      for (int ks = 0; ks < S::KS; ++ks) s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[nb][ks], qb[ks], s[nb], 0, 0, 0);
     }
+
+    // stage V as pair rows: load i holds keys RPI*i + vr, load i + VL/2 the
+    // keys 16 later; one output dword = (key j, key j + 16) of one dim.
+    // (The previous chunk's reads of this wave's buffer are complete: LDS
+    // operations of one wave execute in order.)
     wave_sync();
-    // P.V on the VALU: one gathered V row per step
-#pragma unroll 8
-    for (int kq = 0; kq < kAttnChunk / RG; ++kq) {
-      const int kk = kq * RG + rg;
-      const int vk = __shfl(key, kk, 64);
-      const uint32_t pair = *(const uint32_t*)(vb + (size_t)vk * D + d0);
-      const float v0 = __uint_as_float(pair << 16);
-      const float v1 = __uint_as_float(pair & 0xffff0000u);
-      const f32x4* prow = (const f32x4*)P[kk];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 pp = prow[q4];
+    for (int i = 0; i < S::VL / 2; ++i) {
+      const i32x4 lo = vv[i], hi = vv[i + S::VL / 2];
+      i32x4 x, y;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[4 * q4 + j][0] = __builtin_fmaf(pp[j], v0, o[4 * q4 + j][0]);
-          o[4 * q4 + j][1] = __builtin_fmaf(pp[j], v1, o[4 * q4 + j][1]);
-        }
+      for (int c = 0; c < 2; ++c) {
+        x[2 * c] = __builtin_amdgcn_perm(hi[c], lo[c], 0x05040100u);
+        x[2 * c + 1] = __builtin_amdgcn_perm(hi[c], lo[c], 0x07060302u);
+        y[2 * c] = __builtin_amdgcn_perm(hi[2 + c], lo[2 + c], 0x05040100u);
+        y[2 * c + 1] = __builtin_amdgcn_perm(hi[2 + c], lo[2 + c], 0x07060302u);
       }
+      unsigned char* dst = vl + prow(S::RPI * i + vr) * S::PSTRIDE + 32 * vc;
+      *(i32x4*)dst = x;
+      *(i32x4*)(dst + 16) = y;
     }
+
+    // online softmax for head i16 (replicated over the four lane groups)
+    float sv[8];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * nb + 4 * g + r;
+        const float x = ((vmask >> j) & 1u) ? s[nb][r] * sl2 : -__builtin_inff();
+        sv[4 * nb + r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const bool none = mn == -__builtin_inff();
+    const float corr = none ? 1.0f : exp2_fast(m - mn);
+    // P^T as the B operand; k-slot (g, 2w) is key 4g + w, (g, 2w + 1) key 16 + 4g + w
+    bf16x8 pb;
+    float psum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = none ? 0.0f : exp2_fast(sv[w] - mn);
+      const float p1 = none ? 0.0f : exp2_fast(sv[4 + w] - mn);
+      psum += p0 + p1;
+      pb[2 * w] = (__bf16)p0;
+      pb[2 * w + 1] = (__bf16)p1;
+    }
+    l = l * corr + psum;
+    m = mn;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) o[db] *= corr;
     wave_sync();
-  }
-  // reduce the per-lane partial sums over the 16 keys of each lane group
+
+    // O^T += V^T . P^T with the same k-slot order: dword w of the A operand is
+    // the pair row of pair 4g + w at dim 16*db + i16
 #pragma unroll
-  for (int r = 0; r < 4; ++r) l[r] = wave_sum16(l[r]);
-  if (RG == 2) {
+    for (int db = 0; db < S::DB; ++db) {
+      i32x4 a;
 #pragma unroll
-    for (int h = 0; h < 16; ++h)
-#pragma unroll
-      for (int c = 0; c < DPL; ++c) o[h][c] += __shfl_xor(o[h][c], 32, 64);
-  }
-  const bool writer = (RG == 1) || lane < 32;
-  for (int h = 0; h < p.H; ++h) {
-    const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m[h & 3]), 16 * (h >> 2)));
-    const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l[h & 3]), 16 * (h >> 2)));
-    if constexpr (SPLIT) {
-      float* dst = p.part + (((size_t)row * p.nsplit + split) * p.H + h) * (D + 2);
-      if (writer) {
-        dst[d0] = o[h][0];
-        dst[d0 + 1] = o[h][1];
-      }
-      if (lane == 0) {
-        dst[D] = mh;
-        dst[D + 1] = lh;
-      }
-    } else {
-      const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-      if (writer) {
-        __bf16* dst = (__bf16*)p.out + ((size_t)row * p.H + h) * D + d0;
-        dst[0] = (__bf16)(o[h][0] * inv);
-        dst[1] = (__bf16)(o[h][1] * inv);
-      }
-      if (p.lse && lane == 0)
-        p.lse[(size_t)row * p.H + h] = lh > 0.0f ? (mh + __log2f(lh)) * 0.6931471805599453f
-                                                 : -__builtin_inff();
+      for (int w = 0; w < 4; ++w) a[w] = *(const int*)(vl + prow(4 * g + w) * S::PSTRIDE + 4 * (16 * db + i16));
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[db], 0, 0, 0);
     }
+  }
+  // the four lane groups summed different keys of the same head
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (i16 >= p.H) return;
+  // lane holds O[head i16][16*db + 4*g + r]
+  if constexpr (SPLIT) {
+    float* dst = p.part + ((size_t)wid * p.H + i16) * kAttnPartStride<D>;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) *(f32x4*)(dst + 16 * db + 4 * g) = o[db];
+    if (g == 0) {
+      dst[D] = m;
+      dst[D + 1] = l;
+    }
+  } else {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    __bf16* dst = (__bf16*)p.out + ((size_t)row * p.H + i16) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[db][r] * inv);
+      *(bf16x4*)(dst + 16 * db) = v;
+    }
+    if (p.lse && g == 0)
+      p.lse[(size_t)row * p.H + i16] = l > 0.0f ? (m + __log2f(l)) * 0.6931471805599453f : -__builtin_inff();
   }
 }
 
-// Merges the split partials: M = max_s m_s, L = sum_s l_s 2^(m_s - M),
-// O = sum_s o_s 2^(m_s - M) / L  (m in log2 units).
+// Merges the split partials of one (query, head) per wave:
+// M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s o_s 2^(m_s - M) / L
+// (m in log2 units; splits with no valid entry have m = -inf, l = 0, o = 0).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
-  const int row = blockIdx.x;
-  const int ns = p.nsplit;
-  for (int e = threadIdx.x; e < p.H * D; e += blockDim.x) {
-    const int h = e / D, d = e - h * D;
-    const float* base = p.part + ((size_t)row * ns * p.H + h) * (D + 2);
-    const size_t sstride = (size_t)p.H * (D + 2);
-    float M = -__builtin_inff();
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * sstride + D]);
-    float L = 0.0f, O = 0.0f;
-    if (M != -__builtin_inff()) {
-      for (int s = 0; s < ns; ++s) {
-        const float ms = base[s * sstride + D];
-        const float f = ms == -__builtin_inff() ? 0.0f : exp2f(ms - M);
-        L += base[s * sstride + D + 1] * f;
-        O += base[s * sstride + d] * f;
-      }
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    ((__bf16*)p.out)[((size_t)row * p.H + h) * D + d] = (__bf16)(O * inv);
-    if (p.lse && d == 0)
-      p.lse[(size_t)row * p.H + h] = L > 0.0f ? (M + __log2f(L)) * 0.6931471805599453f : -__builtin_inff();
+  constexpr int DPL = D / kWave;  // output dims per lane
+  const int lane = lane_id();
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.y;
+  if (h >= p.H) return;
+  const int ns = p.nsplit;  // <= 64
+  const size_t sstride = (size_t)p.H * kAttnPartStride<D>;
+  const float* base = p.part + ((size_t)row * ns * p.H + h) * kAttnPartStride<D>;
+  const float ms = lane < ns ? base[lane * sstride + D] : -__builtin_inff();
+  const float ls = lane < ns ? base[lane * sstride + D + 1] : 0.0f;
+  float M = ms;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+  const float f = (ms == -__builtin_inff()) ? 0.0f : exp2_fast(ms - M);
+  float L = ls * f;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) L += __shfl_xor(L, d, 64);
+  float o[DPL];
+#pragma unroll
+  for (int c = 0; c < DPL; ++c) o[c] = 0.0f;
+  const float* src = base + DPL * lane;
+  for (int sp = 0; sp < ns; ++sp) {
+    const float fs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), sp));
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) o[c] = __builtin_fmaf(fs, src[sp * sstride + c], o[c]);
   }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  __bf16* dst = (__bf16*)p.out + ((size_t)row * p.H + h) * D + DPL * lane;
+#pragma unroll
+  for (int c = 0; c < DPL; ++c) dst[c] = (__bf16)(o[c] * inv);
+  if (p.lse && lane == 0)
+    p.lse[(size_t)row * p.H + h] = L > 0.0f ? (M + __log2f(L)) * 0.6931471805599453f : -__builtin_inff();
 }
 
 template <int D>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s) {
   const int rows = p.B * p.n_q;
-  const dim3 grid((rows + kAttnWaves - 1) / kAttnWaves, p.nsplit);
+  const long waves = (long)rows * p.nsplit;
+  const dim3 grid((unsigned)((waves + kAttnWaves - 1) / kAttnWaves));
   if (p.nsplit > 1) {
     hipLaunchKernelGGL((sparse_attn_kernel<D, true>), grid, dim3(kAttnWaves * kWave), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(rows), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((p.H + 3) / 4, rows), dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL((sparse_attn_kernel<D, false>), grid, dim3(kAttnWaves * kWave), 0, s, p);
   }
