@@ -227,6 +227,9 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline + CPU baseline only")
     ap.add_argument("--stack-L", type=int, default=61440)
     ap.add_argument("--stack-layers", type=int, default=47)
+    ap.add_argument("--only", choices=["stack", "decode"], default=None,
+                    help="run only the stack or only the decode measurement and print its JSON "
+                         "(for profiling one part; not the benchmark line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 3 times (reference dispatch for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling) and exit")
@@ -255,6 +258,14 @@ def main():
         print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
         return
     L, H, D, topk = args.L, 64, 128, 2048
+    if args.only == "stack":
+        print(json.dumps(stack_bench(dsa, torch, args.stack_L, args.stack_layers, topk,
+                                     max(1, args.steps // 2), 1)), flush=True)
+        return
+    if args.only == "decode":
+        print(json.dumps({f"decode_B{B}": decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
+                          for B in (1, 32)}), flush=True)
+        return
 
     log(f"generating the L={L} {args.dtype} layer")
     inp = make_indexer_inputs(1, L, L, H, D, config=5, dtype=args.dtype, w_std=0.125, device="cuda")

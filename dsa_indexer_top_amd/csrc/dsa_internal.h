@@ -8,12 +8,15 @@
 
 namespace dsa {
 
-// Candidate-list capacity per query row. Prefill (streaming filter): room
-// for the kept superset of the top-k plus new arrivals; shrinks cost about
-// C / (C - k) list passes per accepted key, so 4k is used. Decode (one
-// threshold pass): 2k.
+// Candidate-list capacity per query row, 4k (at least k + 256), in both
+// paths. Prefill (streaming filter): room for the kept superset of the top-k
+// plus new arrivals; a shrink costs about C / (C - k) list passes per
+// accepted key. Decode (one threshold pass): every key whose 12-bit histogram
+// bin reaches the k-th key's bin, i.e. k plus most of one bin; a larger list
+// sends the request to the exact full-row select.
 inline int cand_capacity(int topk, bool decode) {
-  int c = topk * (decode ? 2 : 4);
+  (void)decode;
+  int c = topk * 4;
   if (c < topk + 256) c = topk + 256;
   return (c + 63) / 64 * 64;
 }
@@ -21,8 +24,9 @@ inline int cand_capacity(int topk, bool decode) {
 // Decode path: bins of the first-level histogram of the 32-bit score keys.
 constexpr int kDecodeHistBits = 12;
 constexpr int kDecodeHistBins = 1 << kDecodeHistBits;
-constexpr int kDecodeKeysPerBlock = 256;
-constexpr int kDecodeCollectBlocks = 64;
+constexpr int kDecodeWaveKeys = 32;          // keys per wave step of the score kernel
+constexpr int kDecodeBlockKeys = 4 * kDecodeWaveKeys;
+constexpr int kDecodeCollectKeys = 4096;     // keys per block of the collect kernel
 
 struct IndexerParams {
   int B, n_q, n_k, pos_offset, H, D, topk, fp8;
@@ -40,7 +44,7 @@ struct IndexerParams {
   int32_t* cand_cnt;    // [rows]
   int C;
   uint32_t* dec_keys;   // decode: [B, n_k] score keys
-  uint32_t* dec_hist;   // decode: [B, kDecodeHistBins]
+  uint32_t* dec_hist;   // decode: [B, kDecodeHistBins], directly followed by cand_cnt
   void* const* ev;      // optional phase events (3): before scores, after scores, after select
 };
 

@@ -251,10 +251,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 #pragma unroll
   for (int c = 0; c < DPL; ++c) o[c] = 0.0f;
   const float* src = base + DPL * lane;
-  for (int sp = 0; sp < ns; ++sp) {
-    const float fs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), sp));
+  // 16 splits per round: all loads of a round are issued before their FMAs
+  for (int s0 = 0; s0 < ns; s0 += 16) {
+    float v[16][DPL];
 #pragma unroll
-    for (int c = 0; c < DPL; ++c) o[c] = __builtin_fmaf(fs, src[sp * sstride + c], o[c]);
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) v[j][c] = s0 + j < ns ? src[(s0 + j) * sstride + c] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int sp = s0 + j < ns ? s0 + j : 0;
+      const float fs = s0 + j < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), sp)) : 0.0f;
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) o[c] = __builtin_fmaf(fs, v[j][c], o[c]);
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   __bf16* dst = (__bf16*)p.out + ((size_t)row * p.H + h) * D + DPL * lane;

@@ -7,12 +7,16 @@
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace dsa {
 
-constexpr int kFinNT = 256;
-constexpr int kFinMax = 4096;  // largest candidate list sorted in LDS
+// Threads per finalize workgroup: a prefill launch has one workgroup per query
+// row and many rows in flight; a decode launch has one per request, so each
+// is made wide to cut its latency (the sort is one barrier per network stage).
+constexpr int kFinNTPrefill = 512;
+constexpr int kFinNTDecode = 1024;
 
 __device__ __forceinline__ uint64_t composite(uint32_t u, int32_t idx) {
   return ((uint64_t)u << 32) | (uint64_t)(~(uint32_t)idx);
@@ -59,12 +63,13 @@ __device__ int block_excl_scan(int v, int* scratch /* >= 17 ints */, int* total)
   return r;
 }
 
-// The k-th largest of keys[0..n) (1 <= k <= n), by 4 radix steps of 8 bits
-// over a 256-bin LDS histogram: *theta = that key, *need = how many keys equal
-// to theta belong to the k largest when ties go to the lowest index.
-// keys may live in LDS or global memory. Called by the whole workgroup.
-__device__ void block_kth_key(const uint32_t* keys, int n, int k, uint32_t* hist, uint32_t* theta,
-                              int* need) {
+// The k-th largest of the keys of the participating entries i < n (get(i, u)
+// returns whether entry i takes part and sets its key u; 1 <= k <= their
+// count), by 4 radix steps of 8 bits over a 256-bin LDS histogram: *theta =
+// that key, *need = how many keys equal to theta belong to the k largest.
+// Called by the whole workgroup.
+template <class Get>
+__device__ void block_kth(Get get, int n, int k, uint32_t* hist, uint32_t* theta, int* need) {
   __shared__ int sh_digit, sh_above;
   uint32_t prefix = 0u, pmask = 0u;
   int remaining = k;
@@ -72,8 +77,8 @@ __device__ void block_kth_key(const uint32_t* keys, int n, int k, uint32_t* hist
     for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint32_t u = keys[i];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      uint32_t u;
+      if (get(i, u) && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (threadIdx.x < kWave) {
@@ -110,6 +115,12 @@ __device__ void block_kth_key(const uint32_t* keys, int n, int k, uint32_t* hist
   }
   *theta = prefix;
   *need = remaining;
+}
+
+// block_kth over every entry of keys[0..n) (LDS or global memory).
+__device__ void block_kth_key(const uint32_t* keys, int n, int k, uint32_t* hist, uint32_t* theta,
+                              int* need) {
+  block_kth([&](int i, uint32_t& u) { u = keys[i]; return true; }, n, k, hist, theta, need);
 }
 
 // Writes, in list order, the composite keys of the entries of keys[0..n) that
@@ -169,14 +180,14 @@ __device__ void pad_and_sort(uint64_t* s, int n_items) {
   block_bitonic_desc(s, n);
 }
 
-// Prefill rows: each candidate list (<= kPrefillMaxC entries, in index order)
+// Prefill rows: each candidate list (<= kMaxC entries, in index order)
 // is a superset of the row's top-k. The exact k-th key is found in LDS, the k
 // winners are collected in list order (ties: lowest index) and sorted.
-constexpr int kPrefillMaxC = 8192;
+constexpr int kMaxC = 8192;
 constexpr int kMaxTopk = 2048;
 
-__global__ __launch_bounds__(kFinNT) void prefill_finalize_kernel(FinalizeParams p) {
-  __shared__ uint32_t skey[kPrefillMaxC];
+__global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(FinalizeParams p) {
+  __shared__ uint32_t skey[kMaxC];
   __shared__ uint64_t s[kMaxTopk];
   __shared__ uint32_t hist[256];
   __shared__ int scratch[17];
@@ -198,25 +209,61 @@ __global__ __launch_bounds__(kFinNT) void prefill_finalize_kernel(FinalizeParams
   write_sorted(p, r, s, take);
 }
 
-// Decode requests: the candidate list (unordered, <= C = kFinMax entries) is
-// sorted whole; if it overflowed, the exact top-k is taken from the request's
-// full key row instead.
-__global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(FinalizeParams p) {
-  __shared__ uint64_t s[kFinMax];
+// Decode requests: the candidate list is unordered (<= C entries, a superset
+// of the top-k). The k-th key theta is found in LDS; if more entries tie at
+// theta than the top-k takes, a second select over their inverted indices
+// keeps the lowest ones. The winners are then sorted. If the list overflowed,
+// the exact top-k is taken from the request's full key row instead.
+__global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeParams p) {
+  __shared__ uint32_t skey[kMaxC];
+  __shared__ uint64_t s[kMaxTopk];
   __shared__ uint32_t hist[256];
   __shared__ int scratch[17];
+  __shared__ int sh_n;
   const int r = blockIdx.x;
   const int t = r % p.n_q;
   const int n_valid = min(p.pos_offset + t + 1, p.n_k);
   const int k_eff = min(p.topk, n_valid);
   const int cnt = p.cand_cnt[r];
-  int n_sorted;
   if (cnt <= p.C) {
     const uint32_t* ck = p.cand_key + (size_t)r * p.C;
     const int32_t* ci = p.cand_idx + (size_t)r * p.C;
-    for (int i = threadIdx.x; i < cnt; i += blockDim.x) s[i] = composite(ck[i], ci[i]);
-    pad_and_sort(s, cnt);
-    n_sorted = min(cnt, k_eff);
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
+    if (threadIdx.x == 0) sh_n = 0;
+    __syncthreads();
+    const int take = min(k_eff, cnt);  // cnt >= k_eff by construction
+    uint32_t theta = 0u;               // below every finite score's key: keep all
+    uint32_t cut = 0u;                 // keep ties with ~index >= cut
+    if (cnt > take) {
+      int need;
+      block_kth_key(skey, cnt, take, hist, &theta, &need);
+      int ties = 0;
+      for (int i = threadIdx.x; i < cnt; i += blockDim.x) ties += skey[i] == theta;
+      int tie_total;
+      block_excl_scan(ties, scratch, &tie_total);
+      if (tie_total > need) {
+        int one;
+        block_kth([&](int i, uint32_t& u) {
+                    u = ~(uint32_t)ci[i];
+                    return skey[i] == theta;
+                  },
+                  cnt, need, hist, &cut, &one);
+      }
+    }
+    for (int i0 = 0; i0 < cnt; i0 += blockDim.x) {
+      const int i = i0 + threadIdx.x;
+      const uint32_t u = i < cnt ? skey[i] : 0u;
+      const int32_t ix = i < cnt ? ci[i] : 0;
+      const bool keep = i < cnt && (u > theta || (u == theta && ~(uint32_t)ix >= cut));
+      const uint64_t m = ballot(keep);
+      int base = 0;
+      if (lane_id() == 0 && m) base = atomicAdd(&sh_n, popc64(m));
+      base = __shfl(base, 0, 64);
+      if (keep) s[base + mbcnt(m)] = composite(u, ix);
+    }
+    __syncthreads();
+    pad_and_sort(s, take);
+    write_sorted(p, r, s, take);
   } else {
     const uint32_t* keys = p.full_keys + (size_t)r * p.n_k;
     uint32_t theta;
@@ -224,9 +271,8 @@ __global__ __launch_bounds__(kFinNT) void decode_finalize_kernel(FinalizeParams 
     block_kth_key(keys, n_valid, k_eff, hist, &theta, &need);
     block_ordered_collect(keys, nullptr, n_valid, theta, need, s, scratch);
     pad_and_sort(s, k_eff);
-    n_sorted = k_eff;
+    write_sorted(p, r, s, k_eff);
   }
-  write_sorted(p, r, s, n_sorted);
 }
 
 hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s) {
@@ -244,9 +290,9 @@ hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s
   p.out_idx = ip.out_idx;
   p.out_scores = ip.out_scores;
   if (ip.n_q == 1)
-    hipLaunchKernelGGL(decode_finalize_kernel, dim3(rows), dim3(kFinNT), 0, s, p);
+    hipLaunchKernelGGL(decode_finalize_kernel, dim3(rows), dim3(kFinNTDecode), 0, s, p);
   else
-    hipLaunchKernelGGL(prefill_finalize_kernel, dim3(rows), dim3(kFinNT), 0, s, p);
+    hipLaunchKernelGGL(prefill_finalize_kernel, dim3(rows), dim3(kFinNTPrefill), 0, s, p);
   return hipGetLastError();
 }
 
@@ -258,25 +304,47 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ a, size_t n, uint32_t v) 
     a[i] = v;
 }
 
-// One query (64 heads max) against 256 keys per workgroup, 64 per wave; the
-// k rows stream straight from HBM into MFMA B-fragments (each row is used
-// once). Writes each causal key's 32-bit order key and adds the block's
-// histogram of the top kDecodeHistBits bits to the request's global histogram.
+// One decode query (up to 64 heads) per request against its key cache. The
+// grid is (blocks per request, B); the four waves of a block take 32-key steps
+// of the block's key range in turn. A step's k rows are read with fully
+// coalesced 16-byte loads (a row's bytes by consecutive lanes) into one of two
+// register buffers, written to the wave's LDS tile (rows padded by 16 bytes
+// so the fragment reads below are bank-conflict free) and read back as MFMA B
+// fragments; the loads of step i + 2 are issued as soon as step i's rows are
+// in LDS, so two steps are in flight while the MFMAs and the epilogue run.
+// Each causal key's 32-bit order key goes to the workspace; the block's
+// histogram of the top kDecodeHistBits bits is kept in LDS and added to the
+// request's global histogram once, at the end.
+template <int D, bool FP8>
+struct DecodeTile {
+  static constexpr int RB = FP8 ? D : 2 * D;        // bytes per key row
+  static constexpr int RS = RB + 16;                // LDS bytes per row
+  static constexpr int LPR = RB / 16;               // lanes per row in a load
+  static constexpr int RPI = kWave / LPR;           // rows per load instruction
+  static constexpr int NI = kDecodeWaveKeys / RPI;  // load instructions per step
+  static constexpr int BYTES = kDecodeWaveKeys * RS;
+  static_assert((RS / 16) % 2 == 1, "16-lane phases of a fragment read must cover distinct banks");
+};
+
 template <int D, int MB, bool FP8, bool DUMP>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
+  using T = DecodeTile<D, FP8>;
   constexpr int KS = FP8 ? D / 64 : D / 16;
-  constexpr int RB = FP8 ? D : 2 * D;  // bytes per key row
+  typedef typename std::conditional<FP8, i32x8, bf16x8>::type Frag;
   __shared__ uint32_t hist[kDecodeHistBins];
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) unsigned char tile[4][T::BYTES];
+  const int lane = lane_id(), wave = uniform_i(threadIdx.x >> 6);
   const int b = blockIdx.y;
   const int i32 = lane & 31, g = lane >> 5;
   const size_t row = (size_t)b * p.n_q;  // n_q == 1
   const int kend = min(p.pos_offset + 1, p.n_k);
-  const int base = blockIdx.x * kDecodeKeysPerBlock + wave * kWave;
+  const int per = ((kend + (int)gridDim.x - 1) / (int)gridDim.x + kDecodeBlockKeys - 1) / kDecodeBlockKeys *
+                  kDecodeBlockKeys;
+  const int k0 = blockIdx.x * per;
+  const int k1 = min(k0 + per, kend);
 
   for (int i = threadIdx.x; i < kDecodeHistBins; i += blockDim.x) hist[i] = 0u;
 
-  typedef typename std::conditional<FP8, i32x8, bf16x8>::type Frag;
   Frag qa[MB][KS];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -308,73 +376,87 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
       const int head = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
       wr[mb][r] = head < p.H ? p.w[row * p.H + head] * qs : 0.0f;
     }
+  __syncthreads();  // histogram cleared
 
-  // B fragments straight from global memory
-  Frag kb[2][KS];
-  const unsigned char* kbase = (const unsigned char*)p.k + (size_t)b * p.n_k * RB;
+  const unsigned char* kbase = (const unsigned char*)p.k + (size_t)b * p.n_k * T::RB;
+  const float* kscale = FP8 ? p.k_scale + (size_t)b * p.n_k : nullptr;
+  uint32_t* keys_out = p.dec_keys + (size_t)b * p.n_k;
+  unsigned char* lt = tile[wave];
+  const int lr = lane / T::LPR, lc = lane % T::LPR;  // load: row in group, 16-byte chunk
+
+  // rows base .. base + 31, coalesced (rows past k1 read row 0, masked later)
+  auto load_step = [&](i32x4 (&buf)[T::NI], float& ksc, int base) {
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int key = base + 32 * nb + i32;
-    const bool ok = key < kend;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (FP8) {
-        i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (ok) {
-          const unsigned char* src = kbase + (size_t)key * RB + g * (D / 2) + 32 * ks;
-          const i32x4 lo = *(const i32x4*)src, hi = *(const i32x4*)(src + 16);
-          v = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        kb[nb][ks] = v;
-      } else {
-        bf16x8 v = {};
-        if (ok) v = *(const bf16x8*)(kbase + (size_t)key * RB + 2 * (g * (D / 2) + 8 * ks));
-        kb[nb][ks] = v;
-      }
+    for (int i = 0; i < T::NI; ++i) {
+      const int key = base + T::RPI * i + lr;
+      buf[i] = *(const i32x4*)(kbase + (size_t)(key < k1 ? key : 0) * T::RB + 16 * lc);
     }
-  }
-  f32x16 acc[MB][2];
+    if constexpr (FP8) {
+      const int key = base + i32;
+      ksc = kscale[key < k1 ? key : 0];
+    }
+  };
+  // one step: rows to LDS, refill the buffer with the step two ahead, MFMAs
+  // on fragments read from LDS, epilogue
+  auto step = [&](i32x4 (&buf)[T::NI], float& ksc, int base) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if constexpr (FP8)
-          acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][ks], kb[nb][ks], acc[mb][nb],
-                                                                       0, 0, 0, 127, 0, 127);
-        else
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb[nb][ks], acc[mb][nb], 0, 0, 0);
-      }
-  float part[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    float s = 0.0f;
+    for (int i = 0; i < T::NI; ++i) *(i32x4*)(lt + (T::RPI * i + lr) * T::RS + 16 * lc) = buf[i];
+    const float ksc_cur = ksc;
+    const int ahead = base + 2 * kDecodeBlockKeys;
+    if (ahead < k1) load_step(buf, ksc, ahead);
+    wave_sync();
+    // B fragment: key base + i32, dims g*(D/2) + (8 bf16 | 32 fp8)*ks ..
+    const unsigned char* fr = lt + i32 * T::RS + (FP8 ? g * (D / 2) : g * D);
+    f32x16 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s = __builtin_fmaf(wr[mb][r], fmaxf(acc[mb][nb][r], 0.0f), s);
-    part[nb] = s;
+      for (int r = 0; r < 16; ++r) acc[mb][r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Frag kb;
+      if constexpr (FP8) {
+        const i32x4 lo = *(const i32x4*)(fr + 32 * ks), hi = *(const i32x4*)(fr + 32 * ks + 16);
+        kb = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        kb = *(const bf16x8*)(fr + 16 * ks);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (FP8)
+          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mb][ks], kb, acc[mb], 0, 0, 0, 127, 0, 127);
+        else
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+      }
+    }
+    // lane holds heads 32*mb + 8(r/4) + 4g + (r%4) of key base + i32
+    float part = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        part = __builtin_fmaf(wr[mb][r], __int_as_float(max(__float_as_int(acc[mb][r]), 0)), part);
+    float score = part + __shfl_xor(part, 32, 64);
+    if constexpr (FP8) score *= ksc_cur;
+    const int key = base + i32;
+    if (g == 0 && key < k1) {
+      const uint32_t u = score_key(score);
+      keys_out[key] = u;
+      if constexpr (DUMP) p.dump[row * (size_t)p.n_k + key] = canon_zero(score);
+      atomicAdd(&hist[u >> (32 - kDecodeHistBits)], 1u);
+    }
+  };
+
+  i32x4 buf0[T::NI], buf1[T::NI];
+  float ksc0 = 0.0f, ksc1 = 0.0f;
+  int base = k0 + kDecodeWaveKeys * wave;
+  if (base < k1) load_step(buf0, ksc0, base);
+  if (base + kDecodeBlockKeys < k1) load_step(buf1, ksc1, base + kDecodeBlockKeys);
+  for (; base < k1; base += 2 * kDecodeBlockKeys) {
+    step(buf0, ksc0, base);
+    if (base + kDecodeBlockKeys >= k1) break;
+    step(buf1, ksc1, base + kDecodeBlockKeys);
   }
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
-                                                   false, false);
-  float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  const int key = base + lane;
-  const bool valid = key < kend;
-  if constexpr (FP8) score *= valid ? p.k_scale[(size_t)b * p.n_k + key] : 0.0f;
-  const uint32_t u = score_key(score);
-  if (valid) {
-    p.dec_keys[(size_t)b * p.n_k + key] = u;
-    if constexpr (DUMP) p.dump[row * (size_t)p.n_k + key] = canon_zero(score);
-  }
-  __syncthreads();
-  if (valid) atomicAdd(&hist[u >> (32 - kDecodeHistBits)], 1u);
   __syncthreads();
   uint32_t* gh = p.dec_hist + (size_t)b * kDecodeHistBins;
   for (int i = threadIdx.x; i < kDecodeHistBins; i += blockDim.x) {
@@ -383,73 +465,88 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
   }
 }
 
-// Threshold bin of one request: the largest bin T with
-// count(bins >= T) >= k_eff. Computed by one wave.
-__device__ int wave_threshold_bin(const uint32_t* __restrict__ gh, int k_eff) {
-  constexpr int PER = kDecodeHistBins / kWave;
-  const int lane = lane_id();
-  const int top = kDecodeHistBins - 1 - PER * lane;  // lane l owns bins top .. top-PER+1
-  uint32_t loc = 0;
-  for (int j = 0; j < PER; ++j) loc += gh[top - j];
-  const uint32_t incl = wave_incl_scan(loc);
-  const uint64_t m = ballot(incl >= (uint32_t)k_eff);
-  const int L = uniform_i(m ? __builtin_ctzll(m) : 63);
-  int bin = 0;
-  if (lane == L) {
-    uint32_t cum = incl - loc;
-    bin = top - PER + 1;
+// Threshold bin of a request's histogram, by the whole (256-thread) block:
+// the largest T with count(bins >= T) >= k_eff.
+__device__ int block_threshold_bin(const uint32_t* __restrict__ gh, int k_eff, int* scratch) {
+  constexpr int PER = kDecodeHistBins / 256;
+  __shared__ int sh_bin;
+  const int top = kDecodeHistBins - 1 - PER * (int)threadIdx.x;  // thread t owns bins top .. top-PER+1
+  uint32_t c[PER];
+  int loc = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = gh[top - j];
+    loc += (int)c[j];
+  }
+  int total;
+  const int before = block_excl_scan(loc, scratch, &total);  // keys in higher bins
+  if (before < k_eff && before + loc >= k_eff) {
+    int cum = before;
+#pragma unroll
     for (int j = 0; j < PER; ++j) {
-      cum += gh[top - j];
-      if (cum >= (uint32_t)k_eff) {
-        bin = top - j;
+      cum += (int)c[j];
+      if (cum >= k_eff) {
+        sh_bin = top - j;
         break;
       }
     }
   }
-  return __builtin_amdgcn_readlane(bin, L);
+  __syncthreads();
+  return sh_bin;
 }
 
 // Appends every key whose top bits reach the threshold bin to the request's
-// candidate list (count may exceed C: the finalize kernel then falls back to
-// an exact full-row select).
+// candidate list, in no particular order (the count may exceed C: the
+// finalize kernel then takes the exact full-row select). One atomic per block
+// reserves the block's slots.
 __global__ __launch_bounds__(256) void decode_collect_kernel(IndexerParams p) {
-  __shared__ int sh_bin;
+  __shared__ int scratch[17];
+  __shared__ int sh_base;
   const int b = blockIdx.y;
   const int n_valid = min(p.pos_offset + 1, p.n_k);
   const int k_eff = min(p.topk, n_valid);
-  if (threadIdx.x < kWave) {
-    const int bin = wave_threshold_bin(p.dec_hist + (size_t)b * kDecodeHistBins, k_eff);
-    if (threadIdx.x == 0) sh_bin = bin;
-  }
-  __syncthreads();
-  const uint32_t tbin = (uint32_t)sh_bin;
-  const int chunk = (n_valid + gridDim.x - 1) / gridDim.x;
-  const int beg = blockIdx.x * chunk, end = min(beg + chunk, n_valid);
+  const uint32_t tbin = (uint32_t)block_threshold_bin(p.dec_hist + (size_t)b * kDecodeHistBins, k_eff, scratch);
+  const int beg = blockIdx.x * kDecodeCollectKeys, end = min(beg + kDecodeCollectKeys, n_valid);
   const uint32_t* keys = p.dec_keys + (size_t)b * p.n_k;
+  constexpr int U = kDecodeCollectKeys / 256;
+  // thread t takes the U consecutive keys beg + U*t ..
+  uint32_t u[U];
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int i = beg + U * (int)threadIdx.x + j;
+    u[j] = i < end ? keys[i] : 0u;
+    n += (i < end && (u[j] >> (32 - kDecodeHistBits)) >= tbin) ? 1 : 0;
+  }
+  int total;
+  int pos = block_excl_scan(n, scratch, &total);
+  if (total == 0) return;
+  if (threadIdx.x == 0) sh_base = atomicAdd(&p.cand_cnt[b], total);
+  __syncthreads();
+  pos += sh_base;
   uint32_t* ck = p.cand_key + (size_t)b * p.C;
   int32_t* ci = p.cand_idx + (size_t)b * p.C;
-  for (int i0 = beg; i0 < end; i0 += blockDim.x) {
-    const int i = i0 + threadIdx.x;
-    const bool in = i < end;
-    const uint32_t u = in ? keys[i] : 0u;
-    const bool sel = in && (u >> (32 - kDecodeHistBits)) >= tbin;
-    const uint64_t m = ballot(sel);
-    if (m) {
-      int basepos = 0;
-      if (lane_id() == 0) basepos = atomicAdd(&p.cand_cnt[b], popc64(m));
-      basepos = __shfl(basepos, 0, 64);
-      const int pos = basepos + mbcnt(m);
-      if (sel && pos < p.C) {
-        ck[pos] = u;
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int i = beg + U * (int)threadIdx.x + j;
+    if (i < end && (u[j] >> (32 - kDecodeHistBits)) >= tbin) {
+      if (pos < p.C) {
+        ck[pos] = u[j];
         ci[pos] = i;
       }
+      ++pos;
     }
   }
 }
 
 template <int D, int MB, bool FP8>
 static void launch_decode_scores_t(const IndexerParams& p, hipStream_t s) {
-  const dim3 grid((p.n_k + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock, p.B);
+  // about 512 blocks in all (two per CU), at least one block step each
+  const int kend = std::min(p.pos_offset + 1, p.n_k);
+  const int steps = (kend + kDecodeBlockKeys - 1) / kDecodeBlockKeys;
+  int nb = 512 / p.B;
+  nb = std::max(1, std::min(nb, steps));
+  const dim3 grid(nb, p.B);
   if (p.dump)
     hipLaunchKernelGGL((indexer_decode_kernel<D, MB, FP8, true>), grid, dim3(256), 0, s, p);
   else
@@ -457,11 +554,11 @@ static void launch_decode_scores_t(const IndexerParams& p, hipStream_t s) {
 }
 
 hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
-  // zero the histograms and candidate counters (a fill kernel, not a memset node)
-  const size_t nh = (size_t)p.B * kDecodeHistBins;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, s, p.dec_hist, nh, 0u);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((p.B + 255) / 256)), dim3(256), 0, s,
-                     (uint32_t*)p.cand_cnt, (size_t)p.B, 0u);
+  // zero the histograms and the candidate counters that follow them (a fill
+  // kernel, not a memset node)
+  const size_t nz = (size_t)p.B * kDecodeHistBins + (size_t)p.B;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 1024)), dim3(256), 0, s,
+                     p.dec_hist, nz, 0u);
   hipError_t e = record_phase(p.ev, 0, s);
   if (e != hipSuccess) return e;
   const bool two = p.H > 32;
@@ -477,7 +574,9 @@ hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   e = record_phase(p.ev, 1, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_collect_kernel, dim3(kDecodeCollectBlocks, p.B), dim3(256), 0, s, p);
+  const int n_valid = std::min(p.pos_offset + 1, p.n_k);
+  const int ncb = (n_valid + kDecodeCollectKeys - 1) / kDecodeCollectKeys;
+  hipLaunchKernelGGL(decode_collect_kernel, dim3(ncb, p.B), dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_topk_finalize(p, p.B, s);
