@@ -123,12 +123,13 @@ __device__ void block_kth_key(const uint32_t* keys, int n, int k, uint32_t* hist
   block_kth([&](int i, uint32_t& u) { u = keys[i]; return true; }, n, k, hist, theta, need);
 }
 
-// Writes, in list order, the composite keys of the entries of keys[0..n) that
-// are > theta plus the first `need` equal to theta, to s[0..). idx[i] is the
-// token index of entry i (NULL: the entry's position). Each thread owns one
-// contiguous segment, so two block-wide scans place every entry.
-__device__ void block_ordered_collect(const uint32_t* keys, const int32_t* __restrict__ idx, int n,
-                                      uint32_t theta, int need, uint64_t* s, int* scratch) {
+// Emits, in list order, the entries of keys[0..n) that are > theta plus the
+// first `need` equal to theta: emit(position, key, token index). idx[i] is
+// the token index of entry i (NULL: the entry's position). Each thread owns
+// one contiguous segment, so two block-wide scans place every entry.
+template <class Emit>
+__device__ void block_ordered_emit(const uint32_t* keys, const int32_t* __restrict__ idx, int n, uint32_t theta,
+                                   int need, int* scratch, Emit emit) {
   const int per = (n + blockDim.x - 1) / blockDim.x;
   const int i0 = min((int)threadIdx.x * per, n), i1 = min(i0 + per, n);
   int ties = 0;
@@ -146,9 +147,93 @@ __device__ void block_ordered_collect(const uint32_t* keys, const int32_t* __res
   for (int i = i0, tr = tie_rank; i < i1; ++i) {
     const uint32_t u = keys[i];
     const bool keep = u > theta || (u == theta && tr++ < need);
-    if (keep) s[pos++] = composite(u, idx ? idx[i] : i);
+    if (keep) emit(pos++, u, idx ? idx[i] : i);
   }
   __syncthreads();
+}
+
+// The same, as composite keys in s[0..).
+__device__ void block_ordered_collect(const uint32_t* keys, const int32_t* __restrict__ idx, int n,
+                                      uint32_t theta, int need, uint64_t* s, int* scratch) {
+  block_ordered_emit(keys, idx, n, theta, need, scratch,
+                     [&](int pos, uint32_t u, int32_t ix) { s[pos] = composite(u, ix); });
+}
+
+// Stable LSD radix sort of kSortN (key, index) pairs in LDS by descending key
+// (equal keys keep their order) by a workgroup of kSortWaves waves. Wave w
+// holds positions 256w + 64j + lane (j < 4) of the current order. Each 8-bit
+// pass ranks every element among the equal digits of its wave (lanes matched
+// by 8 ballots, rows in order, a per-wave histogram carrying the rows before),
+// scans the per-(digit, wave) counts in digit-major order and scatters to the
+// other buffer; after the 4 passes the result is back in (ka, ia).
+// hist: 256 * kSortWaves entries.
+constexpr int kSortWaves = 8;
+constexpr int kSortN = kSortWaves * 256;
+
+__device__ void block_radix_sort_desc(uint32_t* ka, int32_t* ia, uint32_t* kb, int32_t* ib, uint32_t* hist,
+                                      int* scratch) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const uint64_t gt = ~lt & ~(1ull << lane);
+  uint32_t* hw = hist + 256 * w;
+#pragma unroll 1
+  for (int shift = 0; shift < 32; shift += 8) {
+    uint32_t u[4], d[4];
+    int32_t x[4];
+    int rank[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 256 * w + 64 * j + lane;
+      u[j] = ka[e];
+      x[j] = ia[e];
+      d[j] = (~u[j] >> shift) & 255u;  // ascending ~key = descending key
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hw[4 * lane + q] = 0u;
+    wave_sync();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint64_t m = ~0ull;
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool set = (d[j] >> bit) & 1u;
+        const uint64_t bal = ballot(set);
+        m &= set ? bal : ~bal;
+      }
+      rank[j] = (int)hw[d[j]] + popc64(m & lt);
+      wave_sync();
+      if ((m & gt) == 0ull) hw[d[j]] += (uint32_t)popc64(m);  // the group's highest lane
+      wave_sync();
+    }
+    __syncthreads();
+    // thread t owns entries 4t .. 4t+3 of the (digit, wave) order: digit t/2,
+    // waves 4(t&1) .. 4(t&1)+3
+    const int dg = threadIdx.x >> 1, w0 = 4 * (threadIdx.x & 1);
+    uint32_t c[4];
+    int tot = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = hist[256 * (w0 + q) + dg];
+      tot += (int)c[q];
+    }
+    int total;
+    int base = block_excl_scan(tot, scratch, &total);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hist[256 * (w0 + q) + dg] = (uint32_t)base;
+      base += (int)c[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pos = (int)hist[256 * w + d[j]] + rank[j];
+      kb[pos] = u[j];
+      ib[pos] = x[j];
+    }
+    __syncthreads();
+    uint32_t* tk = ka; ka = kb; kb = tk;
+    int32_t* ti = ia; ia = ib; ib = ti;
+  }
 }
 
 struct FinalizeParams {
@@ -187,10 +272,15 @@ constexpr int kMaxC = 8192;
 constexpr int kMaxTopk = 2048;
 
 __global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(FinalizeParams p) {
+  static_assert(kFinNTPrefill == kSortWaves * kWave && kSortN >= kMaxTopk, "sort layout");
+  // skey: the candidate keys; after the collect, the sort's second buffers
+  // and its histograms
   __shared__ uint32_t skey[kMaxC];
-  __shared__ uint64_t s[kMaxTopk];
+  __shared__ uint32_t wkey[kSortN];
+  __shared__ int32_t widx[kSortN];
   __shared__ uint32_t hist[256];
   __shared__ int scratch[17];
+  static_assert(kMaxC >= 2 * kSortN + 256 * kSortWaves, "sort scratch must fit in skey");
   const int r = blockIdx.x;
   const int t = r % p.n_q;
   const int n_valid = min(p.pos_offset + t + 1, p.n_k);
@@ -204,9 +294,25 @@ __global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(Finaliz
   int need = 1 << 30;
   const int take = min(k_eff, cnt);
   if (cnt > take) block_kth_key(skey, cnt, take, hist, &theta, &need);
-  block_ordered_collect(skey, ci, cnt, theta, need, s, scratch);
-  pad_and_sort(s, take);
-  write_sorted(p, r, s, take);
+  // winners in list order, i.e. index order; padding (key 0) sorts last
+  block_ordered_emit(skey, ci, cnt, theta, need, scratch, [&](int pos, uint32_t u, int32_t ix) {
+    wkey[pos] = u;
+    widx[pos] = ix;
+  });
+  for (int i = take + (int)threadIdx.x; i < kSortN; i += blockDim.x) {
+    wkey[i] = 0u;
+    widx[i] = -1;
+  }
+  __syncthreads();
+  // stable by key: equal keys stay in index order, the tie rule
+  block_radix_sort_desc(wkey, widx, skey, (int32_t*)(skey + kSortN), skey + 2 * kSortN, scratch);
+  int32_t* oi = p.out_idx + (size_t)r * p.topk;
+  float* os = p.out_scores ? p.out_scores + (size_t)r * p.topk : nullptr;
+  for (int i = threadIdx.x; i < p.topk; i += blockDim.x) {
+    const bool v = i < take;
+    oi[i] = v ? widx[i] : -1;
+    if (os) os[i] = v ? key_score(wkey[i]) : -__builtin_inff();
+  }
 }
 
 // Decode requests: the candidate list is unordered (<= C entries, a superset
