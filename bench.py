@@ -123,19 +123,24 @@ def cpu_baseline(inp_host, L, topk, budget_s):
                        f"{L} rows by causal-key count (layer estimate {est_s:.0f} s)")}
 
 
-def stack_bench(dsa, torch, L, n_layers, topk, steps, warmup, config=3):
+def stack_bench(dsa, torch, L, n_layers, topk, steps, warmup, config=3, dtype="bf16", patterns=None):
     """47-layer prefill stack, per-layer tensors seeded independently, one shared
-    index buffer; all-F vs index_topk_freq 2 vs 4."""
+    index buffer. patterns: list of (name, run kwargs); default all-F vs
+    index_topk_freq 2 and 4. Reports each pattern's best wall time and mean
+    per-layer event times of its F and S layers."""
     from dsa_inputs import make_attn_inputs, make_indexer_inputs
+    if patterns is None:
+        patterns = [("all_F", {}), ("freq2", {"freq": 2}), ("freq4", {"freq": 4})]
     layers = []
     for l in range(n_layers):
-        ii = make_indexer_inputs(1, L, L, 64, 128, config=config, layer=l, w_std=0.125, device="cuda")
+        ii = make_indexer_inputs(1, L, L, 64, 128, config=config, layer=l, dtype=dtype, w_std=0.125,
+                                 device="cuda")
         aa = make_attn_inputs(1, L, L, 16, 128, config=config, layer=l, device="cuda")
-        layers.append(dict(q_idx=ii.q, k_idx=ii.k, w=ii.w, q_scale=None, k_scale=None,
+        layers.append(dict(q_idx=ii.q, k_idx=ii.k, w=ii.w, q_scale=ii.q_scale, k_scale=ii.k_scale,
                            q=aa.q, k=aa.k, v=aa.v))
     st = dsa.LayerStack(layers, topk, shared_out=True, events=True)
     res = {}
-    for name, kw in (("all_F", {}), ("freq2", {"freq": 2}), ("freq4", {"freq": 4})):
+    for name, kw in patterns:
         for _ in range(warmup):
             st.run(**kw)
         torch.cuda.synchronize()
@@ -146,14 +151,14 @@ def stack_bench(dsa, torch, L, n_layers, topk, steps, warmup, config=3):
             torch.cuda.synchronize()
             times.append(time.perf_counter() - t0)
             per_layer = st.layer_times_ms()
-        pat = dsa.resolve_pattern(n_layers, None, kw.get("freq", 0))
+        pat = dsa.resolve_pattern(n_layers, kw.get("pattern"), kw.get("freq", 0))
         f_ms = [t for t, c in zip(per_layer, pat) if c == "F"]
         s_ms = [t for t, c in zip(per_layer, pat) if c == "S"]
-        res[name] = {"pattern_F": pat.count("F"), "time_s": min(times),
+        res[name] = {"pattern": pat, "pattern_F": pat.count("F"), "time_s": min(times),
                      "mean_F_layer_ms": sum(f_ms) / len(f_ms),
                      "mean_S_layer_ms": (sum(s_ms) / len(s_ms)) if s_ms else None}
-        log(f"stack {name}: {min(times):.3f} s")
-    for name in ("freq2", "freq4"):
+        log(f"stack L={L} {name}: {min(times):.3f} s")
+    for name, _ in patterns[1:]:
         res[name]["speedup_vs_all_F"] = res["all_F"]["time_s"] / res[name]["time_s"]
     del st, layers
     torch.cuda.empty_cache()
@@ -214,6 +219,16 @@ def decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, config=4):
     return res
 
 
+def stack200k(dsa, torch, L, topk, args):
+    """The 47-layer stack at L = 200000 with the fp8 indexer: all-F vs a seeded
+    pattern with 12 F layers (layer 0 and 11 of layers 1..46)."""
+    from dsa_inputs import seeded_pattern
+    pat = seeded_pattern(47, 12, seed=1_000_000 * 5 + 9)
+    return {"L": L, "layers": 47, "dtype": "fp8 indexer, bf16 attention", "attn": "16 heads, d=128, 1 KV head",
+            **stack_bench(dsa, torch, L, 47, topk, 1, 1, config=5, dtype="fp8",
+                          patterns=[("all_F", {}), ("seeded_quarter_F", {"pattern": pat})])}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,7 +242,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline + CPU baseline only")
     ap.add_argument("--stack-L", type=int, default=61440)
     ap.add_argument("--stack-layers", type=int, default=47)
-    ap.add_argument("--only", choices=["stack", "decode"], default=None,
+    ap.add_argument("--only", choices=["stack", "stack200k", "decode"], default=None,
                     help="run only the stack or only the decode measurement and print its JSON "
                          "(for profiling one part; not the benchmark line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -261,6 +276,9 @@ def main():
     if args.only == "stack":
         print(json.dumps(stack_bench(dsa, torch, args.stack_L, args.stack_layers, topk,
                                      max(1, args.steps // 2), 1)), flush=True)
+        return
+    if args.only == "stack200k":
+        print(json.dumps(stack200k(dsa, torch, L, topk, args)), flush=True)
         return
     if args.only == "decode":
         print(json.dumps({f"decode_B{B}": decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
@@ -329,6 +347,8 @@ def main():
                                   "attn": "16 heads, d=128, 1 KV head",
                                   **stack_bench(dsa, torch, args.stack_L, args.stack_layers, topk,
                                                 max(1, args.steps // 2), 1)}
+        log(f"stack prefill L={L}, 47 layers, fp8 indexer")
+        extra["stack_prefill_200k"] = stack200k(dsa, torch, L, topk, args)
         for B in (1, 32):
             log(f"decode B={B}")
             extra[f"decode_B{B}"] = decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
