@@ -31,6 +31,10 @@ Pinning status (what each function is checked against, besides itself):
   pattern.resolve_pattern    README examples (freq 2, freq 4, GLM-5 string, default)
   stack.run_stack            cached-index invariants (S == preceding F, all-F ==
                              per layer, freq 1 == default)
+  quant.e4m3fn_encode        torch's float32 -> float8_e4m3fn cast (library) on
+                             grids with every midpoint; extremes
+  quant.quantize_rows_fp8    the row maximum maps to +-448; dequantisation error
+                             within half a step; zero rows
 No function is "parity unpinned".
 """
 from .formats import bf16_to_f64, e4m3fn_table, e4m3fn_to_f64  # noqa: F401
@@ -44,3 +48,4 @@ from .indexer import (  # noqa: F401
 from .attention import sparse_attention, sparse_attention_rows  # noqa: F401
 from .pattern import resolve_pattern, PatternError  # noqa: F401
 from .stack import run_stack  # noqa: F401
+from .quant import e4m3fn_encode, quantize_rows_fp8  # noqa: F401
