@@ -219,6 +219,29 @@ def decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, config=4):
     return res
 
 
+def quant_bench(dsa, torch, L, steps):
+    """Per-token fp8 quantisation of the 200K layer's q_idx ([L, 64 * 128] bf16):
+    algorithmic HBM bytes = 2 read + 1 written per element + 4 per row."""
+    g = torch.Generator(device="cuda").manual_seed(1_000_000 * 5 + 1)
+    x = torch.randn(L, 64 * 128, generator=g, device="cuda", dtype=torch.bfloat16)
+    codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device="cuda")
+    scale = torch.empty(L, dtype=torch.float32, device="cuda")
+    dsa.quantize_fp8_rows(x, out=codes, scale=scale)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        dsa.quantize_fp8_rows(x, out=codes, scale=scale)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = x.numel() * 3 + L * 4
+    del x, codes, scale
+    torch.cuda.empty_cache()
+    return {"rows": L, "cols": 64 * 128, "ms": ms, "hbm_GBps": nbytes / ms / 1e6,
+            "hbm_frac": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+
+
 def stack200k(dsa, torch, L, topk, args):
     """The 47-layer stack at L = 200000 with the fp8 indexer: all-F vs a seeded
     pattern with 12 F layers (layer 0 and 11 of layers 1..46)."""
@@ -242,7 +265,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline + CPU baseline only")
     ap.add_argument("--stack-L", type=int, default=61440)
     ap.add_argument("--stack-layers", type=int, default=47)
-    ap.add_argument("--only", choices=["stack", "stack200k", "decode"], default=None,
+    ap.add_argument("--only", choices=["stack", "stack200k", "decode", "quant"], default=None,
                     help="run only the stack or only the decode measurement and print its JSON "
                          "(for profiling one part; not the benchmark line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -276,6 +299,9 @@ def main():
     if args.only == "stack":
         print(json.dumps(stack_bench(dsa, torch, args.stack_L, args.stack_layers, topk,
                                      max(1, args.steps // 2), 1)), flush=True)
+        return
+    if args.only == "quant":
+        print(json.dumps(quant_bench(dsa, torch, L, max(2, args.steps))), flush=True)
         return
     if args.only == "stack200k":
         print(json.dumps(stack200k(dsa, torch, L, topk, args)), flush=True)
@@ -347,6 +373,9 @@ def main():
                                   "attn": "16 heads, d=128, 1 KV head",
                                   **stack_bench(dsa, torch, args.stack_L, args.stack_layers, topk,
                                                 max(1, args.steps // 2), 1)}
+        extra["quantize_fp8_q_idx"] = quant_bench(dsa, torch, L, max(2, args.steps))
+        log(f"quantize q_idx: {extra['quantize_fp8_q_idx']['ms']:.3f} ms "
+            f"({extra['quantize_fp8_q_idx']['hbm_GBps']:.0f} GB/s)")
         log(f"stack prefill L={L}, 47 layers, fp8 indexer")
         extra["stack_prefill_200k"] = stack200k(dsa, torch, L, topk, args)
         for B in (1, 32):

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     attn_workspace_size,
     indexer_scores_topk,
     indexer_workspace_size,
+    quantize_fp8_rows,
     resolve_pattern,
     sparse_attn,
 )

@@ -27,6 +27,7 @@ EXPORTS = (
     "dsa_indexer_scores_topk",
     "dsa_sparse_attn",
     "dsa_layer_stack_run",
+    "dsa_quantize_fp8_rows",
     "dsa_status_string",
     "dsa_last_error",
 )
@@ -103,6 +104,8 @@ def load() -> ctypes.CDLL:
     lib.dsa_sparse_attn.argtypes = [POINTER(AttnArgs), c_void_p]
     lib.dsa_layer_stack_run.restype = c_int32
     lib.dsa_layer_stack_run.argtypes = [POINTER(StackArgs), c_char_p, c_int32, c_void_p]
+    lib.dsa_quantize_fp8_rows.restype = c_int32
+    lib.dsa_quantize_fp8_rows.argtypes = [c_void_p, ctypes.c_int64, c_int32, c_void_p, c_void_p, c_void_p]
     lib.dsa_status_string.restype = c_char_p
     lib.dsa_status_string.argtypes = [c_int32]
     lib.dsa_last_error.restype = c_char_p

@@ -233,6 +233,27 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Te
     return out, lse_t
 
 
+def quantize_fp8_rows(x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                      scale: Optional[torch.Tensor] = None, stream=None):
+    """Per-token fp8 quantisation (dsa_quantize_fp8_rows): x is bf16 with the
+    token's values in its last dims, given as [..., cols] (q_idx [B, n_q, H, D]
+    -> pass x.view(B, n_q, H * D); k_idx [B, n_k, D] as is). Returns (codes as
+    float8_e4m3fn with x's shape, scale fp32 with x's shape minus the last dim)."""
+    _need(x, "x", dtype=torch.bfloat16)
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if scale is None:
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _need(out, "out", dtype=torch.float8_e4m3fn)
+    _need(scale, "scale", dtype=torch.float32)
+    if tuple(out.shape) != tuple(x.shape) or scale.numel() != rows:
+        raise ValueError("out must have x's shape and scale one entry per row")
+    _check(L.load().dsa_quantize_fp8_rows(_ptr(x), rows, cols, _ptr(out), _ptr(scale), _stream(stream)))
+    return out, scale
+
+
 def _event_array(events, n):
     """Host array of hipEvent_t handles from torch.cuda.Event objects (or None)."""
     if events is None:

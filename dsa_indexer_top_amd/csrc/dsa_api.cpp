@@ -364,6 +364,23 @@ dsa_status dsa_sparse_attn(const dsa_attn_args* a, void* stream) {
   return st == DSA_OK ? ok() : st;
 }
 
+dsa_status dsa_quantize_fp8_rows(const void* x, int64_t rows, int32_t cols, void* out, float* scale, void* stream) {
+  const char* what = "quantize_fp8_rows";
+  if (rows < 0) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: rows=%lld must be >= 0", what, (long long)rows);
+  if (cols < 8 || cols % 8 != 0 || cols > (1 << 24))
+    return fail(DSA_ERR_UNSUPPORTED, "%s: cols=%d must be a positive multiple of 8, at most 2^24", what, cols);
+  size_t n;
+  if (__builtin_mul_overflow((size_t)rows, (size_t)cols, &n) || n > ((size_t)1 << 62))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: rows * cols overflows", what);
+  if (rows == 0) return ok();
+  if (!x || !out || !scale) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: x, out and scale are required", what);
+  if (!aligned(x, 16) || !aligned(out, 8) || !aligned(scale, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: misaligned pointer (x 16 B, out 8 B, scale 4 B)", what);
+  const hipError_t e = dsa::launch_quantize_fp8_rows(x, rows, cols, out, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
 dsa_status dsa_layer_stack_run(const dsa_stack_args* a, const char* pattern, int32_t freq, void* stream) {
   const char* what = "layer_stack_run";
   dsa_status st = check_stack_shape(a, what);

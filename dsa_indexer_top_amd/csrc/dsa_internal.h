@@ -83,5 +83,6 @@ void indexer_bind_workspace(IndexerParams& p, void* ws);
 hipError_t launch_indexer_prefill(const IndexerParams& p, hipStream_t s);
 hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_quantize_fp8_rows(const void* x, int64_t rows, int cols, void* out, float* scale, hipStream_t s);
 
 }  // namespace dsa

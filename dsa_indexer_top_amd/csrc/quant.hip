@@ -1,0 +1,92 @@
+// Per-token fp8 quantisation of indexer inputs (bf16 -> OCP e4m3fn codes plus
+// one fp32 scale per row):
+//   scale = fl32(amax / 448) (1 for an all-zero row),
+//   code  = e4m3fn(fl32(x / scale)), round to nearest, ties to the even
+//           mantissa, magnitudes clamped to 448.
+// One wave per row: amax is a wave max over the row, then every value is
+// divided, clamped to +-448 (the largest finite e4m3fn magnitude) and
+// converted by v_cvt_pk_fp8_f32 (OCP e4m3fn, round to nearest even on gfx950;
+// the clamp keeps it away from its out-of-range results), 8 codes per lane.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+constexpr int kQuantWaves = 4;
+
+// Rows of up to kQuantRegCols values stay in registers (all of a lane's loads
+// in flight at once, one pass over memory); longer rows take two passes.
+constexpr int kQuantRegChunks = 16;
+constexpr int kQuantRegCols = 8 * kWave * kQuantRegChunks;
+
+// 8 codes: the hardware pair conversion (round to nearest even) after the
+// clamp to +-448, so it never sees an out-of-range value
+__device__ __forceinline__ uint2 encode8(const bf16x8& v, float s) {
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = __builtin_fminf(__builtin_fmaxf((float)v[j] / s, -448.0f), 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+__device__ __forceinline__ float wave_amax(float a) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) a = fmaxf(a, __shfl_xor(a, d, 64));
+  return a;
+}
+
+__global__ __launch_bounds__(kQuantWaves * kWave) void quantize_fp8_rows_kernel(const __bf16* __restrict__ x,
+                                                                                  int64_t rows, int cols,
+                                                                                  uint8_t* __restrict__ out,
+                                                                                  float* __restrict__ scale) {
+  const int lane = lane_id();
+  const int64_t r = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const __bf16* xr = x + r * cols;
+  uint8_t* orow = out + r * cols;
+  if (cols <= kQuantRegCols) {
+    bf16x8 v[kQuantRegChunks];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kQuantRegChunks; ++i) {
+      const int c = 8 * lane + 8 * kWave * i;
+      v[i] = c < cols ? *(const bf16x8*)(xr + c) : (bf16x8){};
+    }
+#pragma unroll
+    for (int i = 0; i < kQuantRegChunks; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf((float)v[i][j]));
+    amax = wave_amax(amax);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE binary32 division
+    if (lane == 0) scale[r] = s;
+#pragma unroll
+    for (int i = 0; i < kQuantRegChunks; ++i) {
+      const int c = 8 * lane + 8 * kWave * i;
+      if (c < cols) *(uint2*)(orow + c) = encode8(v[i], s);
+    }
+    return;
+  }
+  float amax = 0.0f;
+  for (int c = 8 * lane; c < cols; c += 8 * kWave) {
+    const bf16x8 v = *(const bf16x8*)(xr + c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf((float)v[j]));
+  }
+  amax = wave_amax(amax);
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (lane == 0) scale[r] = s;
+  for (int c = 8 * lane; c < cols; c += 8 * kWave) *(uint2*)(orow + c) = encode8(*(const bf16x8*)(xr + c), s);
+}
+
+hipError_t launch_quantize_fp8_rows(const void* x, int64_t rows, int cols, void* out, float* scale, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows + kQuantWaves - 1) / kQuantWaves;
+  hipLaunchKernelGGL(quantize_fp8_rows_kernel, dim3((unsigned)blocks), dim3(kQuantWaves * kWave), 0, s,
+                     (const __bf16*)x, rows, cols, (uint8_t*)out, scale);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -212,6 +212,24 @@ dsa_status dsa_sparse_attn(const dsa_attn_args *args, void *stream);
 dsa_status dsa_layer_stack_run(const dsa_stack_args *args, const char *pattern,
                                int32_t index_topk_freq, void *stream);
 
+/* Per-token fp8 quantisation of indexer inputs: the step that produces the
+ * fp8 e4m3 q_idx / k_idx with per-token fp32 scales that the long-context
+ * configuration feeds dsa_indexer_scores_topk (IndexCache paper page,
+ * configuration of the 200K fp8 runs; the pages do not give the quantiser).
+ * For each row r of x (bf16, [rows, cols] row-major; a token's values: for
+ * q_idx [B, n_q, H, D] one row is one query token, cols = H * D, for k_idx one
+ * key token, cols = D):
+ *   amax = max_c |x[r,c]|, scale[r] = fl32(amax / 448) (1 if amax == 0),
+ *   out[r,c] = e4m3fn(fl32(x[r,c] / scale[r])), round to nearest, ties to the
+ *              even mantissa, magnitudes above 448 clamped to 448 (never NaN),
+ * fl32 = IEEE binary32 rounding. Dequantisation is e4m3fn(out) * scale.
+ * x: device, 16-byte aligned; out: device [rows, cols] bytes (OCP e4m3fn codes),
+ * 8-byte aligned; scale: device [rows] fp32. rows >= 0 (0 = nothing to do);
+ * cols a positive multiple of 8, at most 1 << 24. Inputs must be finite.
+ * Asynchronous on stream; on a validation error nothing is written. */
+dsa_status dsa_quantize_fp8_rows(const void *x, int64_t rows, int32_t cols, void *out, float *scale,
+                                 void *stream);
+
 /* Static text of a status code. */
 const char *dsa_status_string(dsa_status status);
 

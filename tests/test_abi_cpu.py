@@ -26,7 +26,7 @@ def lib():
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "dsa.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -187,3 +187,16 @@ def test_stack_validation(lib):
     assert lib.dsa_stack_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
     assert n.value == max(dsa.indexer_workspace_size(1, 64, 64, 4, 32, 16),
                           dsa.attn_workspace_size(1, 64, 64, 4, 64, 16))
+
+
+def test_quantize_validation(lib):
+    FAKE = 1 << 20  # aligned, never dereferenced: validation fails first
+    q = lib.dsa_quantize_fp8_rows
+    assert q(FAKE, -1, 128, FAKE, FAKE, None) == L.DSA_ERR_INVALID_ARGUMENT
+    assert q(FAKE, 4, 100, FAKE, FAKE, None) == L.DSA_ERR_UNSUPPORTED          # not a multiple of 8
+    assert q(FAKE, 4, 0, FAKE, FAKE, None) == L.DSA_ERR_UNSUPPORTED
+    assert q(FAKE, 4, (1 << 24) + 8, FAKE, FAKE, None) == L.DSA_ERR_UNSUPPORTED
+    assert q(None, 4, 128, FAKE, FAKE, None) == L.DSA_ERR_INVALID_ARGUMENT
+    assert q(FAKE + 8, 4, 128, FAKE, FAKE, None) == L.DSA_ERR_INVALID_ARGUMENT  # x not 16-byte aligned
+    assert q(FAKE, 4, 128, FAKE + 4, FAKE, None) == L.DSA_ERR_INVALID_ARGUMENT  # out not 8-byte aligned
+    assert q(FAKE, 0, 128, None, None, None) == L.DSA_OK                        # nothing to do, no launch
