@@ -7,7 +7,7 @@
 // product), and keeps, per query row, a candidate list that provably contains
 // the row's top-k. The score matrix only ever lives in registers.
 //
-// Mapping (gfx950, wave64). A workgroup owns 8 consecutive query rows, one per
+// Mapping (gfx950, wave64). A workgroup owns 8 (fp8: 4) consecutive query rows, one per
 // wave. A wave holds its row's indexer queries as MFMA A-fragments in
 // registers (heads are the M dimension, padded to 32 or 64 rows) and streams
 // 64-key tiles of k through double-buffered, padded LDS (keys are the N
@@ -36,7 +36,13 @@
 
 namespace dsa {
 
-constexpr int kPrefillWaves = 8;
+// Waves (query rows) per workgroup: fp8 uses 4 (two workgroups per CU, so
+// one can run its MFMAs while the other waits at its per-tile barrier); bf16
+// uses 8 (with 256 threads its K-tile staging would need twice the registers
+// per thread and spill).
+template <bool FP8>
+constexpr int prefill_waves() { return FP8 ? 4 : 8; }
+constexpr int kMaxPrefillWaves = 8;
 constexpr int kTileKeys = 64;
 
 template <int D, bool FP8>
@@ -55,15 +61,16 @@ constexpr int kShrinkHistCopies = 8;  // interleaved copies: clustered keys woul
 
 struct ShrinkLds {
   uint32_t hist[256 * kShrinkHistCopies];
-  int scan[kPrefillWaves + 1];
+  int scan[kMaxPrefillWaves + 1];
   int res[4];                       // digit, keys above the digit, keys in the digit
   uint32_t flags[2];                // bit w: the row of wave w needs a shrink (by parity)
-  int cnt[kPrefillWaves];           // that row's list length (in), new length (out)
-  uint32_t theta[kPrefillWaves];    // new acceptance threshold (out)
+  int cnt[kMaxPrefillWaves];        // that row's list length (in), new length (out)
+  uint32_t theta[kMaxPrefillWaves]; // new acceptance threshold (out)
 };
 
 // Exclusive prefix sum over the workgroup (one value per thread, list order =
 // thread order); *total = sum. Contains barriers: call from every thread.
+template <int W>
 __device__ int coop_excl_scan(int v, ShrinkLds& sh, int* total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan((uint32_t)v);
@@ -71,7 +78,7 @@ __device__ int coop_excl_scan(int v, ShrinkLds& sh, int* total) {
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kPrefillWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     const int x = sh.scan[w];
     before += w < wave ? x : 0;
     all += x;
@@ -86,9 +93,10 @@ __device__ int coop_excl_scan(int v, ShrinkLds& sh, int* total) {
 // histogram (4 keys in flight per thread), wave 0 finds the digit holding the
 // rem-th largest such key. Returns the digit; *above / *in_d = matching keys
 // with a larger digit / with this digit.
+template <int W>
 __device__ int coop_digit_step(const uint32_t* __restrict__ keys, int cnt, uint32_t prefix, uint32_t pmask,
                                int shift, uint32_t rem, ShrinkLds& sh, uint32_t* above, uint32_t* in_d) {
-  constexpr int NT = kPrefillWaves * kWave;
+  constexpr int NT = W * kWave;
   for (int i = threadIdx.x; i < 256 * kShrinkHistCopies; i += NT) sh.hist[i] = 0u;
   __syncthreads();
   const uint32_t copy = threadIdx.x % kShrinkHistCopies;
@@ -155,9 +163,10 @@ __device__ int coop_digit_step(const uint32_t* __restrict__ keys, int cnt, uint3
 // Each thread owns CE consecutive entries of a round; all of a round is read
 // before any of it is written (the scans hold barriers), and a round only
 // writes below its own end.
+template <int W>
 __device__ int coop_compact(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, int cnt, uint32_t theta,
                             int ties_left, ShrinkLds& sh) {
-  constexpr int NT = kPrefillWaves * kWave;
+  constexpr int NT = W * kWave;
   constexpr int CE = 4;
   int out = 0, ties = 0;
 #pragma unroll 1
@@ -174,7 +183,7 @@ __device__ int coop_compact(uint32_t* __restrict__ keys, int32_t* __restrict__ i
       nt += (in && u[j] == theta) ? 1 : 0;
     }
     int tie_total;
-    int tr = ties + coop_excl_scan(nt, sh, &tie_total);
+    int tr = ties + coop_excl_scan<W>(nt, sh, &tie_total);
     int nk = 0;
     uint32_t keep = 0u;
 #pragma unroll
@@ -185,7 +194,7 @@ __device__ int coop_compact(uint32_t* __restrict__ keys, int32_t* __restrict__ i
       nk += kj ? 1 : 0;
     }
     int keep_total;
-    int pos = out + coop_excl_scan(nk, sh, &keep_total);
+    int pos = out + coop_excl_scan<W>(nk, sh, &keep_total);
 #pragma unroll
     for (int j = 0; j < CE; ++j) {
       if ((keep >> j) & 1u) {
@@ -212,6 +221,7 @@ __device__ int coop_compact(uint32_t* __restrict__ keys, int32_t* __restrict__ i
 // If that keeps too many (heavy ties), two more digit steps give the exact
 // k-th key theta and the list keeps exactly k entries: those > theta and the
 // lowest-index ties (the list is in index order).
+template <int W>
 __device__ __forceinline__ void coop_shrink(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, int cnt, int k,
                                             int keep_max, ShrinkLds& sh, uint32_t* theta_out, int* cnt_out) {
   uint32_t prefix = 0u, pmask = 0u;
@@ -221,14 +231,14 @@ __device__ __forceinline__ void coop_shrink(uint32_t* __restrict__ keys, int32_t
   for (int st = 0; st < 4; ++st) {
     uint32_t above, in_d;
     const int shift = 24 - 8 * st;
-    const int d = coop_digit_step(keys, cnt, prefix, pmask, shift, rem, sh, &above, &in_d);
+    const int d = coop_digit_step<W>(keys, cnt, prefix, pmask, shift, rem, sh, &above, &in_d);
     rem -= above;
     prefix |= (uint32_t)d << shift;
     pmask |= 0xFFu << shift;
     if (st == 1 && (int)((uint32_t)k - rem + in_d) <= keep_max) break;  // keys with prefix >= P fit
     if (st == 3) ties_left = (int)rem;
   }
-  const int n = coop_compact(keys, idxs, cnt, prefix, ties_left, sh);
+  const int n = coop_compact<W>(keys, idxs, cnt, prefix, ties_left, sh);
   if (threadIdx.x == 0) {
     *theta_out = prefix;
     *cnt_out = n;
@@ -236,7 +246,9 @@ __device__ __forceinline__ void coop_shrink(uint32_t* __restrict__ keys, int32_t
 }
 
 template <int D, int MB, bool FP8, bool DUMP>
-__global__ __launch_bounds__(kPrefillWaves * kWave) void indexer_prefill_kernel(IndexerParams p) {
+__global__ __launch_bounds__(prefill_waves<FP8>() * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void indexer_prefill_kernel(IndexerParams p) {
+  constexpr int kPrefillWaves = prefill_waves<FP8>();
   using T = KTile<D, FP8>;
   constexpr int NT = kPrefillWaves * kWave;
   constexpr int KS = FP8 ? D / 64 : D / 16;  // MFMA k-steps over head_dim
@@ -453,7 +465,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void indexer_prefill_kernel(
     for (int w = 0; w < kPrefillWaves; ++w) {
       if (!((flags >> w) & 1u) || shl.cnt[w] <= p.C - 3 * kTileKeys) continue;
       const size_t rw = (size_t)b * p.n_q + qb * kPrefillWaves + w;
-      coop_shrink(p.cand_key + rw * p.C, p.cand_idx + rw * p.C, shl.cnt[w], p.topk, p.C - 3 * kTileKeys, shl,
+      coop_shrink<kPrefillWaves>(p.cand_key + rw * p.C, p.cand_idx + rw * p.C, shl.cnt[w], p.topk, p.C - 3 * kTileKeys, shl,
                   &shl.theta[w], &shl.cnt[w]);
       __syncthreads();
     }
@@ -556,8 +568,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void indexer_prefill_kernel(
 
 template <int D, int MB, bool FP8>
 static hipError_t launch_prefill_t(const IndexerParams& p, hipStream_t s) {
-  const dim3 grid((p.n_q + kPrefillWaves - 1) / kPrefillWaves, p.B);
-  const dim3 block(kPrefillWaves * kWave);
+  constexpr int W = prefill_waves<FP8>();
+  const dim3 grid((p.n_q + W - 1) / W, p.B);
+  const dim3 block(W * kWave);
   if (p.dump)
     hipLaunchKernelGGL((indexer_prefill_kernel<D, MB, FP8, true>), grid, block, 0, s, p);
   else
