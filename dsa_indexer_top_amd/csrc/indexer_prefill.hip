@@ -10,7 +10,7 @@
 // Mapping (gfx950, wave64). A workgroup owns 8 (fp8: 4) consecutive query rows, one per
 // wave. A wave holds its row's indexer queries as MFMA A-fragments in
 // registers (heads are the M dimension, padded to 32 or 64 rows) and streams
-// 64-key tiles of k through double-buffered, padded LDS (keys are the N
+// 64-key tiles of k through double-buffered, swizzled LDS (keys are the N
 // dimension, head_dim the K dimension). v_mfma_f32_32x32x16_bf16 (fp8:
 // v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales) produces a 32 heads x 32
 // keys block per lane group; in that layout a lane holds 16 heads of one key,
@@ -48,13 +48,24 @@ constexpr int kTileKeys = 64;
 template <int D, bool FP8>
 struct KTile {
   static constexpr int kRowBytes = FP8 ? D : 2 * D;
-  // +16 bytes per row: the 16-byte reads of 16 consecutive rows then hit 16
-  // distinct groups of 4 LDS banks.
-  static constexpr int kLdsRow = kRowBytes + 16;
   static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kChunks = kTileKeys * kChunksPerRow;
-  static constexpr int kBytes = kTileKeys * kLdsRow;
+  static constexpr int kBytes = kTileKeys * kRowBytes;
+  // Rows are unpadded (a direct global->LDS load fills 1 KB of consecutive
+  // LDS); 16-byte chunk c of row r sits at position c ^ swz(r). Rows that
+  // share one 256-byte bank line take different swizzles, so the 16-byte
+  // fragment reads of 16 consecutive rows hit 16 distinct groups of 4 banks.
+  static constexpr int kRowsPerLine = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
+  static __device__ __forceinline__ int swz(int r) { return (r / kRowsPerLine) & (kChunksPerRow - 1); }
 };
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (the LDS address must be the same for the whole wave). A
+// plain device function: the host pass cannot see this builtin inside the
+// kernel's lambdas.
+__device__ __forceinline__ void lds_load16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
 
 // Workgroup-shared scratch of the cooperative list shrink.
 constexpr int kShrinkHistCopies = 8;  // interleaved copies: clustered keys would serialise one copy
@@ -308,37 +319,26 @@ void indexer_prefill_kernel(IndexerParams p) {
       wr[mb][r] = (active && head < p.H) ? p.w[row * p.H + head] * qs : 0.0f;
     }
 
-  // ---- K tile staging: global -> registers -> LDS
-  // Two register stages: the fetch of tile t+2 is issued right after the
-  // barrier that publishes tile t+1 and only stored to LDS one full iteration
-  // later, so L2/MALL latency hides behind a whole tile of MFMA work.
-  // bf16 with 64 heads and head_dim 128 keeps 64 VGPRs of A fragments; it
-  // uses one stage (fetch issued half an iteration ahead) to stay spill-free.
-  constexpr int NSTAGE = (!FP8 && D == 128 && MB == 2) ? 1 : 2;
-  i32x4 stage0[CPT], stage1[NSTAGE == 2 ? CPT : 1];
+  // ---- K tile staging: global -> LDS directly (global_load_lds_dwordx4).
+  // Tile t lives in lds_k[t & 1]; it is read in the second half of iteration
+  // t - 1 and the first half of iteration t, so its buffer is free after the
+  // barrier of iteration t, when the load of tile t + 2 is issued; the wait
+  // before the barrier of iteration t + 1 completes it, a whole tile of MFMA
+  // work later. No registers hold the tile on the way.
   const unsigned char* kbase = (const unsigned char*)p.k + (size_t)b * p.n_k * T::kRowBytes;
-  // chunk c of this thread: row ch / kChunksPerRow, column ch % kChunksPerRow
-  // (recomputed per use: cheaper than keeping 3 * CPT registers alive)
-  auto ld_row = [&](int c) {
-    const int ch = threadIdx.x + c * NT;
-    return ch < T::kChunks ? ch / T::kChunksPerRow : (1 << 30);
-  };
-  auto ld_col = [&](int c) { return (int)(threadIdx.x + c * NT) % T::kChunksPerRow; };
-  auto load_tile = [&](auto& st, int tile) {
+  auto dma_tile = [&](int tile, int buf) {
     const unsigned char* src = kbase + (size_t)tile * kTileKeys * T::kRowBytes;
+    const int rows_left = p.n_k - tile * kTileKeys;  // >= 1 for every tile < n_tiles
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      i32x4 v = {0, 0, 0, 0};
-      const int r = ld_row(c);
-      if (tile * kTileKeys + r < p.n_k) v = *(const i32x4*)(src + r * T::kRowBytes + ld_col(c) * 16);
-      st[c] = v;
-    }
-  };
-  auto store_tile = [&](const auto& st, int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int r = ld_row(c);
-      if (r < kTileKeys) *(i32x4*)(&lds_k[buf][r * T::kLdsRow + ld_col(c) * 16]) = st[c];
+      const int q0 = c * NT + wave * kWave;  // first 16-byte slot of this wave's load (uniform)
+      if (q0 < T::kChunks) {
+        const int q = q0 + lane;
+        const int r = q / T::kChunksPerRow;
+        const int col = (q % T::kChunksPerRow) ^ T::swz(r);
+        const int rr = r < rows_left ? r : rows_left - 1;  // rows past n_k repeat the last (masked later)
+        lds_load16(src + (size_t)rr * T::kRowBytes + 16 * col, &lds_k[buf][16 * q0]);
+      }
     }
   };
 
@@ -358,14 +358,17 @@ void indexer_prefill_kernel(IndexerParams p) {
   // over its 16 * MB heads (0 when EPI is false).
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type BFrag;
   constexpr int EPK = (16 * MB + KS - 1) / KS;  // epilogue elements per k-step
-  auto read_b = [&](const unsigned char* src0, int ks) -> BFrag {
+  // B fragment of row r (key), k-step ks: dims g*(D/2) + (8 bf16 | 32 fp8)*ks ..
+  auto read_b = [&](const unsigned char* kt, int r, int ks) -> BFrag {
+    const unsigned char* row = kt + r * T::kRowBytes;
+    const int sw = T::swz(r);
     if constexpr (FP8) {
-      const unsigned char* src = src0 + g * (D / 2) + 32 * ks;
-      const i32x4 lo = *(const i32x4*)src;
-      const i32x4 hi = *(const i32x4*)(src + 16);
+      const int c = g * (D / 32) + 2 * ks;
+      const i32x4 lo = *(const i32x4*)(row + 16 * (c ^ sw));
+      const i32x4 hi = *(const i32x4*)(row + 16 * ((c + 1) ^ sw));
       return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     } else {
-      return *(const bf16x8*)(src0 + g * D + 16 * ks);
+      return *(const bf16x8*)(row + 16 * ((g * (D / 16) + ks) ^ sw));
     }
   };
   constexpr int SIDE_KS = KS > 1 ? 1 : 0;  // chunk that also carries the previous tile's filter
@@ -373,17 +376,17 @@ void indexer_prefill_kernel(IndexerParams p) {
                        const f32x16 (&prev)[MB], auto&& side) -> float {
     constexpr bool EPI = decltype(EPI_T)::value;
     constexpr bool MMA = decltype(MMA_T)::value;
-    const unsigned char* src0 = kt + (32 * nb + i32) * T::kLdsRow;
+    const int brow = 32 * nb + i32;
     BFrag bf[3];
     if constexpr (MMA) {
-      bf[0] = read_b(src0, 0);
-      if (KS > 1) bf[1 % 3] = read_b(src0, KS > 1 ? 1 : 0);
+      bf[0] = read_b(kt, brow, 0);
+      if (KS > 1) bf[1 % 3] = read_b(kt, brow, KS > 1 ? 1 : 0);
     }
     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if constexpr (MMA) {
-        if (ks + 2 < KS) bf[(ks + 2) % 3] = read_b(src0, ks + 2);
+        if (ks + 2 < KS) bf[(ks + 2) % 3] = read_b(kt, brow, ks + 2);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           if constexpr (FP8)
@@ -481,13 +484,8 @@ void indexer_prefill_kernel(IndexerParams p) {
   auto no_side = [&]() {};
 
   f32x16 accA[MB], accB[MB];
-  if (n_tiles > 0) {
-    load_tile(stage0, 0);
-    store_tile(stage0, 0);
-  }
-  if constexpr (NSTAGE == 2) {
-    if (n_tiles > 1) load_tile(stage1, 1);
-  }
+  if (n_tiles > 0) dma_tile(0, 0);
+  if (n_tiles > 1) dma_tile(1, 1);
   if (threadIdx.x == 0) {
     shl.flags[0] = 0u;
     shl.flags[1] = 0u;
@@ -498,15 +496,12 @@ void indexer_prefill_kernel(IndexerParams p) {
   __syncthreads();
   if (kend > 0) half_step(FalseT{}, TrueT{}, lds_k[0], 0, accA, accB, no_side);
   // One tile: second half-tile of `tile` (+ epilogue of its first half, + the
-  // previous tile's filter), then publish tile+1 (held in st_next) and start
-  // fetching tile+2 into st_free, then the first half of tile+1 (+ epilogue of
-  // tile's second half); `tile` is then pending for the filter.
-  auto iteration = [&](int tile, auto& st_next, auto& st_free) {
+  // previous tile's filter), then the barrier that publishes tile+1, the load
+  // of tile+2 into the buffer `tile` leaves, then the first half of tile+1
+  // (+ epilogue of tile's second half); `tile` is then pending for the filter.
+  auto iteration = [&](int tile) {
     const int cur = tile & 1;
     const bool more = tile + 1 < n_tiles;
-    if constexpr (NSTAGE == 1) {
-      if (more) load_tile(stage0, tile + 1);
-    }
     const int base = tile * kTileKeys;
     const bool mine = base < kend;                          // wave-uniform
     const bool mine_next = more && base + kTileKeys < kend;
@@ -516,11 +511,8 @@ void indexer_prefill_kernel(IndexerParams p) {
     const int par = tile & 1;
     if (mine) part0 = half_step(TrueT{}, TrueT{}, lds_k[cur], 1, accB, accA, filter_compute);
     else filter_compute();
-    if constexpr (NSTAGE == 1) {
-      if (more) store_tile(stage0, cur ^ 1);
-    } else {
-      if (more) store_tile(st_next, cur ^ 1);
-    }
+    // this wave's load of tile+1 (issued one iteration ago) must have landed
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Appends go out right after the barrier: the next wait on the vector
     // memory counter (for the next K tile) is then half a tile away, so the
@@ -531,9 +523,7 @@ void indexer_prefill_kernel(IndexerParams p) {
     // it (the word is next written two iterations later, after a barrier).
     uint32_t flags_v = 0u;
     auto read_flags = [&]() { flags_v = shl.flags[par ^ 1]; };
-    if constexpr (NSTAGE == 2) {
-      if (tile + 2 < n_tiles) load_tile(st_free, tile + 2);
-    }
+    if (tile + 2 < n_tiles) dma_tile(tile + 2, cur);
     if (mine) {
       if (mine_next)
         part1 = half_step(TrueT{}, TrueT{}, lds_k[cur ^ 1], 0, accA, accB, read_flags);
@@ -549,14 +539,7 @@ void indexer_prefill_kernel(IndexerParams p) {
     }
     coop_shrinks(uniform_u(flags_v), par ^ 1);
   };
-  if constexpr (NSTAGE == 2) {
-    for (int tile = 0; tile < n_tiles; tile += 2) {
-      iteration(tile, stage1, stage0);
-      if (tile + 1 < n_tiles) iteration(tile + 1, stage0, stage1);
-    }
-  } else {
-    for (int tile = 0; tile < n_tiles; ++tile) iteration(tile, stage0, stage0);
-  }
+  for (int tile = 0; tile < n_tiles; ++tile) iteration(tile);
   filter_compute();
   __syncthreads();
   filter_commit(n_tiles & 1);
