@@ -7,7 +7,7 @@
 // product), and keeps, per query row, a candidate list that provably contains
 // the row's top-k. The score matrix only ever lives in registers.
 //
-// Mapping (gfx950, wave64). A workgroup owns 8 (fp8: 4) consecutive query rows, one per
+// Mapping (gfx950, wave64). A workgroup owns 4 consecutive query rows, one per
 // wave. A wave holds its row's indexer queries as MFMA A-fragments in
 // registers (heads are the M dimension, padded to 32 or 64 rows) and streams
 // 64-key tiles of k through double-buffered, swizzled LDS (keys are the N
@@ -36,12 +36,11 @@
 
 namespace dsa {
 
-// Waves (query rows) per workgroup: fp8 uses 4 (two workgroups per CU, so
-// one can run its MFMAs while the other waits at its per-tile barrier); bf16
-// uses 8 (with 256 threads its K-tile staging would need twice the registers
-// per thread and spill).
+// Waves (query rows) per workgroup: 4, so two workgroups share a CU and one
+// can run its MFMAs while the other waits at its per-tile barrier (the K tile
+// goes straight to LDS, so a smaller workgroup costs no staging registers).
 template <bool FP8>
-constexpr int prefill_waves() { return FP8 ? 4 : 8; }
+constexpr int prefill_waves() { return 4; }
 constexpr int kMaxPrefillWaves = 8;
 constexpr int kTileKeys = 64;
 
