@@ -10,7 +10,7 @@
 // Mapping (gfx950, wave64). A workgroup owns 4 consecutive query rows, one per
 // wave. A wave holds its row's indexer queries as MFMA A-fragments in
 // registers (heads are the M dimension, padded to 32 or 64 rows) and streams
-// 64-key tiles of k through double-buffered, swizzled LDS (keys are the N
+// 64-key tiles of k through double-buffered, padded LDS (keys are the N
 // dimension, head_dim the K dimension). v_mfma_f32_32x32x16_bf16 (fp8:
 // v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales) produces a 32 heads x 32
 // keys block per lane group; in that layout a lane holds 16 heads of one key,
@@ -48,14 +48,14 @@ template <int D, bool FP8>
 struct KTile {
   static constexpr int kRowBytes = FP8 ? D : 2 * D;
   static constexpr int kChunksPerRow = kRowBytes / 16;
-  static constexpr int kChunks = kTileKeys * kChunksPerRow;
-  static constexpr int kBytes = kTileKeys * kRowBytes;
-  // Rows are unpadded (a direct global->LDS load fills 1 KB of consecutive
-  // LDS); 16-byte chunk c of row r sits at position c ^ swz(r). Rows that
-  // share one 256-byte bank line take different swizzles, so the 16-byte
-  // fragment reads of 16 consecutive rows hit 16 distinct groups of 4 banks.
-  static constexpr int kRowsPerLine = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
-  static __device__ __forceinline__ int swz(int r) { return (r / kRowsPerLine) & (kChunksPerRow - 1); }
+  // +16 bytes per row: the 16-byte reads of 16 consecutive rows hit 16
+  // distinct groups of 4 LDS banks, and a row's fragment reads are immediate
+  // offsets from its address. A direct load fills 64 consecutive 16-byte
+  // slots; lanes whose slot is a row's padding load nothing.
+  static constexpr int kLdsRow = kRowBytes + 16;
+  static constexpr int kSlotsPerRow = kChunksPerRow + 1;
+  static constexpr int kSlots = kTileKeys * kSlotsPerRow;
+  static constexpr int kBytes = kTileKeys * kLdsRow;
 };
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
@@ -262,7 +262,7 @@ void indexer_prefill_kernel(IndexerParams p) {
   using T = KTile<D, FP8>;
   constexpr int NT = kPrefillWaves * kWave;
   constexpr int KS = FP8 ? D / 64 : D / 16;  // MFMA k-steps over head_dim
-  constexpr int CPT = (T::kChunks + NT - 1) / NT;
+  constexpr int CPT = (T::kSlots + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][T::kBytes];
   __shared__ ShrinkLds shl;
 
@@ -327,16 +327,17 @@ void indexer_prefill_kernel(IndexerParams p) {
   const unsigned char* kbase = (const unsigned char*)p.k + (size_t)b * p.n_k * T::kRowBytes;
   auto dma_tile = [&](int tile, int buf) {
     const unsigned char* src = kbase + (size_t)tile * kTileKeys * T::kRowBytes;
-    const int rows_left = p.n_k - tile * kTileKeys;  // >= 1 for every tile < n_tiles
+    const int rows_left = p.n_k - tile * kTileKeys;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int q0 = c * NT + wave * kWave;  // first 16-byte slot of this wave's load (uniform)
-      if (q0 < T::kChunks) {
+      const int q0 = c * NT + wave * kWave;  // first 16-byte LDS slot of this wave's load (uniform)
+      if (q0 < T::kSlots) {
         const int q = q0 + lane;
-        const int r = q / T::kChunksPerRow;
-        const int col = (q % T::kChunksPerRow) ^ T::swz(r);
+        const int r = q / T::kSlotsPerRow;
+        const int col = q - r * T::kSlotsPerRow;
         const int rr = r < rows_left ? r : rows_left - 1;  // rows past n_k repeat the last (masked later)
-        lds_load16(src + (size_t)rr * T::kRowBytes + 16 * col, &lds_k[buf][16 * q0]);
+        if (col < T::kChunksPerRow && r < kTileKeys)
+          lds_load16(src + (size_t)rr * T::kRowBytes + 16 * col, &lds_k[buf][16 * q0]);
       }
     }
   };
@@ -358,18 +359,19 @@ void indexer_prefill_kernel(IndexerParams p) {
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type BFrag;
   constexpr int EPK = (16 * MB + KS - 1) / KS;  // epilogue elements per k-step
   // B fragment of row r (key), k-step ks: dims g*(D/2) + (8 bf16 | 32 fp8)*ks ..
+  // B fragment of row r (key), k-step ks: dims g*(D/2) + (8 bf16 | 32 fp8)*ks ..
   auto read_b = [&](const unsigned char* kt, int r, int ks) -> BFrag {
-    const unsigned char* row = kt + r * T::kRowBytes;
-    const int sw = T::swz(r);
+    const unsigned char* row = kt + r * T::kLdsRow;
     if constexpr (FP8) {
-      const int c = g * (D / 32) + 2 * ks;
-      const i32x4 lo = *(const i32x4*)(row + 16 * (c ^ sw));
-      const i32x4 hi = *(const i32x4*)(row + 16 * ((c + 1) ^ sw));
+      const unsigned char* src = row + g * (D / 2) + 32 * ks;
+      const i32x4 lo = *(const i32x4*)src;
+      const i32x4 hi = *(const i32x4*)(src + 16);
       return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     } else {
-      return *(const bf16x8*)(row + 16 * ((g * (D / 16) + ks) ^ sw));
+      return *(const bf16x8*)(row + g * D + 16 * ks);
     }
   };
+
   constexpr int SIDE_KS = KS > 1 ? 1 : 0;  // chunk that also carries the previous tile's filter
   auto half_step = [&](auto EPI_T, auto MMA_T, const unsigned char* kt, int nb, f32x16 (&acc)[MB],
                        const f32x16 (&prev)[MB], auto&& side) -> float {
