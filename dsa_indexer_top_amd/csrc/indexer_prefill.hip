@@ -359,7 +359,6 @@ void indexer_prefill_kernel(IndexerParams p) {
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type BFrag;
   constexpr int EPK = (16 * MB + KS - 1) / KS;  // epilogue elements per k-step
   // B fragment of row r (key), k-step ks: dims g*(D/2) + (8 bf16 | 32 fp8)*ks ..
-  // B fragment of row r (key), k-step ks: dims g*(D/2) + (8 bf16 | 32 fp8)*ks ..
   auto read_b = [&](const unsigned char* kt, int r, int ks) -> BFrag {
     const unsigned char* row = kt + r * T::kLdsRow;
     if constexpr (FP8) {
