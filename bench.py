@@ -13,7 +13,8 @@ causal triangle only), timed live with HIP events recorded by the library on
 the stream it launches on. `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same layer's query rows and extrapolates by the number of
 causal keys. `extra` adds the bf16 200K layer, the 47-layer F/S prefill stack at
-L = 61440 (all-F, index_topk_freq 2 and 4) and decode at 200K context.
+L = 61440 (all-F, index_topk_freq 2 and 4), decode at 200K context and paged
+decode of 32 requests with ragged context lengths up to 200K.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -219,6 +220,68 @@ def decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, config=4):
     return res
 
 
+def paged_decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, page_size=64, config=6):
+    """One decode token of B requests with seeded ragged context lengths
+    (uniform in [2048, T]) over paged pools (page_size tokens, pages handed out
+    in a seeded random order), 47 layers with the seeded 12-F pattern; two
+    distinct layer sets rotate. Pools hold N(0,1) draws: the rows are the
+    requests' caches. Algorithmic indexer bytes = sum of lengths * (256 k_idx
+    bytes + 4 score-key bytes)."""
+    import numpy as np
+    from dsa_inputs import make_paged_layout, seeded_pattern, seed_for, randn
+    rng = np.random.default_rng(1_000_000 * config + 11)
+    lens = rng.integers(2048, T + 1, size=B)
+    lay = make_paged_layout(lens.tolist(), page_size, T, seed=1_000_000 * config + 12).to("cuda")
+    kv = dsa.PagedKV(lay.seq_lens, lay.block_table, page_size, lay.num_pages, T)
+    sets = []
+    for l in range(2):
+        def pool(name, D=128):
+            return randn((lay.num_pages, page_size, D), seed_for(config, l, name), "cuda").to(torch.bfloat16)
+        q_idx = randn((B, 1, 64, 128), seed_for(config, l, "q_idx"), "cuda").to(torch.bfloat16)
+        w = randn((B, 1, 64), seed_for(config, l, "w"), "cuda") * 0.125
+        q = randn((B, 1, 16, 128), seed_for(config, l, "q"), "cuda").to(torch.bfloat16)
+        sets.append(dict(q_idx=q_idx, k_idx=pool("k_idx"), w=w, q_scale=None, k_scale=None,
+                         q=q, k=pool("k"), v=pool("v")))
+    layers = [sets[l % 2] for l in range(n_layers)]
+    pat = seeded_pattern(n_layers, 12, seed=1_000_000 * config + 9)
+    l0 = sets[0]
+    evi = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    eva = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    k_ms = a_ms = 0.0
+    for i in range(warmup + steps):
+        r = dsa.paged_indexer_topk(l0["q_idx"], l0["k_idx"], l0["w"], topk, kv, phase_events=evi)
+        dsa.paged_sparse_attn(l0["q"], l0["k"], l0["v"], r.idx, kv, phase_events=eva)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            k_ms += evi[0].elapsed_time(evi[1]) / steps
+            a_ms += eva[0].elapsed_time(eva[1]) / steps
+    total = int(lens.sum())
+    idx_bytes = total * (128 * 2 + 4)
+    att_bytes = B * topk * 2 * 128 * 2
+    st = dsa.LayerStack(layers, topk, shared_out=True, kv=kv)
+    for _ in range(warmup):
+        st.run(pat)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        st.run(pat)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    step = min(times)
+    res = {"B": B, "max_context": T, "page_size": page_size, "context_sum": total,
+           "context_mean": total / B, "pattern": pat,
+           "indexer_kernel_ms": k_ms, "indexer_hbm_GBps": idx_bytes / k_ms / 1e6,
+           "indexer_hbm_frac": idx_bytes / k_ms / 1e6 / PEAK_HBM_GBS,
+           "attn_ms": a_ms, "attn_gather_GBps": att_bytes / a_ms / 1e6,
+           "step_ms_47_layers": step * 1e3, "tok_per_s_total": B / step}
+    log(f"paged decode B={B} (mean context {total / B:.0f}): indexer {k_ms:.3f} ms "
+        f"({res['indexer_hbm_GBps']:.0f} GB/s), attn {a_ms:.3f} ms, 47-layer step {step*1e3:.2f} ms")
+    del st, layers, sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def quant_bench(dsa, torch, L, steps):
     """Per-token fp8 quantisation of the 200K layer's q_idx ([L, 64 * 128] bf16):
     algorithmic HBM bytes = 2 read + 1 written per element + 4 per row."""
@@ -265,7 +328,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline + CPU baseline only")
     ap.add_argument("--stack-L", type=int, default=61440)
     ap.add_argument("--stack-layers", type=int, default=47)
-    ap.add_argument("--only", choices=["stack", "stack200k", "decode", "quant"], default=None,
+    ap.add_argument("--only", choices=["stack", "stack200k", "decode", "paged", "quant"], default=None,
                     help="run only the stack or only the decode measurement and print its JSON "
                          "(for profiling one part; not the benchmark line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -309,6 +372,9 @@ def main():
     if args.only == "decode":
         print(json.dumps({f"decode_B{B}": decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
                           for B in (1, 32)}), flush=True)
+        return
+    if args.only == "paged":
+        print(json.dumps(paged_decode_bench(dsa, torch, 32, 200000, 47, topk, args.steps, 2)), flush=True)
         return
 
     log(f"generating the L={L} {args.dtype} layer")
@@ -381,6 +447,8 @@ def main():
         for B in (1, 32):
             log(f"decode B={B}")
             extra[f"decode_B{B}"] = decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
+        log("paged ragged decode B=32")
+        extra["decode_paged_ragged_B32"] = paged_decode_bench(dsa, torch, 32, 200000, 47, topk, args.steps, 2)
         result["extra"] = extra
     print(json.dumps(result), flush=True)
 

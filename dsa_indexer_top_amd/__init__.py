@@ -10,10 +10,14 @@ from .api import (  # noqa: F401
     DsaError,
     IndexerResult,
     LayerStack,
+    PagedKV,
     abi_version,
     attn_workspace_size,
     indexer_scores_topk,
     indexer_workspace_size,
+    paged_append_rows,
+    paged_indexer_topk,
+    paged_sparse_attn,
     quantize_fp8_rows,
     resolve_pattern,
     sparse_attn,

@@ -28,6 +28,10 @@ EXPORTS = (
     "dsa_sparse_attn",
     "dsa_layer_stack_run",
     "dsa_quantize_fp8_rows",
+    "dsa_paged_indexer_topk",
+    "dsa_paged_sparse_attn",
+    "dsa_paged_layer_stack_run",
+    "dsa_paged_append_rows",
     "dsa_status_string",
     "dsa_last_error",
 )
@@ -57,6 +61,14 @@ class AttnArgs(ctypes.Structure):
         ("out", c_void_p), ("lse", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("phase_events", c_void_p),
+    ]
+
+
+class PagedKVArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_uint32),
+        ("max_seq_len", c_int32), ("page_size", c_int32), ("max_pages", c_int32), ("num_pages", c_int32),
+        ("seq_lens", c_void_p), ("block_table", c_void_p),
     ]
 
 
@@ -104,6 +116,14 @@ def load() -> ctypes.CDLL:
     lib.dsa_sparse_attn.argtypes = [POINTER(AttnArgs), c_void_p]
     lib.dsa_layer_stack_run.restype = c_int32
     lib.dsa_layer_stack_run.argtypes = [POINTER(StackArgs), c_char_p, c_int32, c_void_p]
+    lib.dsa_paged_indexer_topk.restype = c_int32
+    lib.dsa_paged_indexer_topk.argtypes = [POINTER(IndexerArgs), POINTER(PagedKVArgs), c_void_p]
+    lib.dsa_paged_sparse_attn.restype = c_int32
+    lib.dsa_paged_sparse_attn.argtypes = [POINTER(AttnArgs), POINTER(PagedKVArgs), c_void_p]
+    lib.dsa_paged_layer_stack_run.restype = c_int32
+    lib.dsa_paged_layer_stack_run.argtypes = [POINTER(StackArgs), POINTER(PagedKVArgs), c_char_p, c_int32, c_void_p]
+    lib.dsa_paged_append_rows.restype = c_int32
+    lib.dsa_paged_append_rows.argtypes = [c_void_p, c_int32, c_int32, c_void_p, POINTER(PagedKVArgs), c_void_p]
     lib.dsa_quantize_fp8_rows.restype = c_int32
     lib.dsa_quantize_fp8_rows.argtypes = [c_void_p, ctypes.c_int64, c_int32, c_void_p, c_void_p, c_void_p]
     lib.dsa_status_string.restype = c_char_p

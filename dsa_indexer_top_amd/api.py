@@ -233,6 +233,136 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Te
     return out, lse_t
 
 
+class PagedKV:
+    """Layout of a paged, ragged decode cache (dsa_paged_kv): request b has
+    seq_lens[b] tokens and token s sits in page block_table[b, s // page_size],
+    slot s % page_size, of each page pool ([num_pages, page_size, ...]).
+    seq_lens [B] and block_table [B, max_pages] are int32 GPU tensors;
+    max_seq_len is a host upper bound of seq_lens."""
+
+    def __init__(self, seq_lens: torch.Tensor, block_table: torch.Tensor, page_size: int, num_pages: int,
+                 max_seq_len: int):
+        _need(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+        _need(block_table, "block_table", dtype=torch.int32, ndim=2)
+        if block_table.shape[0] != seq_lens.shape[0]:
+            raise ValueError("block_table must be [B, max_pages]")
+        self.seq_lens, self.block_table = seq_lens, block_table
+        self.page_size, self.num_pages, self.max_seq_len = int(page_size), int(num_pages), int(max_seq_len)
+        self.B, self.max_pages = block_table.shape
+        a = L.PagedKVArgs()
+        a.struct_size = ctypes.sizeof(L.PagedKVArgs)
+        a.max_seq_len, a.page_size = self.max_seq_len, self.page_size
+        a.max_pages, a.num_pages = self.max_pages, self.num_pages
+        a.seq_lens, a.block_table = _ptr(seq_lens), _ptr(block_table)
+        self.args = a
+
+    def check_pool(self, pool: torch.Tensor, name: str, row_shape):
+        if tuple(pool.shape) != (self.num_pages, self.page_size, *row_shape):
+            raise ValueError(f"{name} must be [num_pages, page_size, {', '.join(map(str, row_shape))}]")
+
+
+def paged_indexer_topk(q: torch.Tensor, k_pool: torch.Tensor, w: torch.Tensor, topk: int, kv: PagedKV, *,
+                       q_scale: Optional[torch.Tensor] = None, k_scale_pool: Optional[torch.Tensor] = None,
+                       out_idx: Optional[torch.Tensor] = None, out_scores=False, debug_full_scores=False,
+                       workspace: Optional[torch.Tensor] = None, stream=None,
+                       phase_events=None) -> IndexerResult:
+    """Decode indexer + top-k over a paged cache (dsa_paged_indexer_topk).
+    q [B, 1, H, D], w [B, 1, H], k_pool [num_pages, page_size, D] (bf16 or
+    float8_e4m3fn); fp8: q_scale [B, 1], k_scale_pool [num_pages, page_size].
+    Indices are logical token positions; debug_full_scores is [B, 1, max_seq_len]."""
+    _need(q, "q", ndim=4)
+    B, n_q, H, D = q.shape
+    if n_q != 1 or B != kv.B:
+        raise ValueError("q must be [B, 1, H, D] with B = kv.B")
+    _need(k_pool, "k_pool", dtype=q.dtype)
+    kv.check_pool(k_pool, "k_pool", (D,))
+    _need(w, "w", dtype=torch.float32, ndim=3)
+    if tuple(w.shape) != (B, 1, H):
+        raise ValueError("w must be [B, 1, H]")
+    code = _dtype_code(q)
+    if code == L.DSA_FP8_E4M3FN:
+        _need(q_scale, "q_scale", dtype=torch.float32, ndim=2)
+        _need(k_scale_pool, "k_scale_pool", dtype=torch.float32, ndim=2)
+        kv.check_pool(k_scale_pool, "k_scale_pool", ())
+        if tuple(q_scale.shape) != (B, 1):
+            raise ValueError("q_scale must be [B, 1]")
+    dev = q.device
+    n_k = kv.max_seq_len
+    if out_idx is None:
+        out_idx = torch.empty((B, 1, topk), dtype=torch.int32, device=dev)
+    else:
+        _need(out_idx, "out_idx", dtype=torch.int32)
+        if tuple(out_idx.shape) != (B, 1, topk):
+            raise ValueError("out_idx must be [B, 1, topk]")
+    sc = torch.empty((B, 1, topk), dtype=torch.float32, device=dev) if out_scores is True else (
+        out_scores if isinstance(out_scores, torch.Tensor) else None)
+    full = torch.full((B, 1, n_k), float("nan"), dtype=torch.float32, device=dev) if debug_full_scores is True \
+        else (debug_full_scores if isinstance(debug_full_scores, torch.Tensor) else None)
+    a = indexer_args(B, 1, n_k, n_k - 1, H, D, topk, code)
+    nbytes = ctypes.c_size_t(0)
+    _check(L.load().dsa_indexer_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws = _workspace(int(nbytes.value), dev, workspace)
+    a.q, a.k, a.w = _ptr(q), _ptr(k_pool), _ptr(w)
+    a.q_scale, a.k_scale = _ptr(q_scale), _ptr(k_scale_pool)
+    a.out_idx, a.out_scores, a.debug_full_scores = _ptr(out_idx), _ptr(sc), _ptr(full)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    keep = _event_array(phase_events, 3)
+    a.phase_events = None if keep is None else ctypes.cast(keep, ctypes.c_void_p)
+    _check(L.load().dsa_paged_indexer_topk(ctypes.byref(a), ctypes.byref(kv.args), _stream(stream)))
+    return IndexerResult(out_idx, sc, full)
+
+
+def paged_sparse_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, idx: torch.Tensor,
+                      kv: PagedKV, *, scale: float = 0.0, out: Optional[torch.Tensor] = None, lse=False,
+                      workspace: Optional[torch.Tensor] = None, stream=None, phase_events=None):
+    """Decode sparse attention over a paged cache (dsa_paged_sparse_attn): q
+    [B, 1, H, D], k_pool / v_pool [num_pages, page_size, D] bf16, idx [B, 1, topk]
+    logical positions. Returns (out [B, 1, H, D] bf16, lse or None)."""
+    _need(q, "q", dtype=torch.bfloat16, ndim=4)
+    B, n_q, H, D = q.shape
+    if n_q != 1 or B != kv.B:
+        raise ValueError("q must be [B, 1, H, D] with B = kv.B")
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _need(t, nm, dtype=torch.bfloat16)
+        kv.check_pool(t, nm, (D,))
+    _need(idx, "idx", dtype=torch.int32, ndim=3)
+    if idx.shape[0] != B or idx.shape[1] != 1:
+        raise ValueError("idx must be [B, 1, topk]")
+    topk = idx.shape[2]
+    dev = q.device
+    n_k = kv.max_seq_len
+    if out is None:
+        out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=dev)
+    lse_t = torch.empty((B, 1, H), dtype=torch.float32, device=dev) if lse is True else (
+        lse if isinstance(lse, torch.Tensor) else None)
+    a = attn_args(B, 1, n_k, n_k - 1, H, D, topk, scale)
+    nbytes = ctypes.c_size_t(0)
+    _check(L.load().dsa_attn_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws = _workspace(int(nbytes.value), dev, workspace)
+    a.q, a.k, a.v, a.idx, a.out, a.lse = _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(idx), _ptr(out), _ptr(lse_t)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    keep = _event_array(phase_events, 2)
+    a.phase_events = None if keep is None else ctypes.cast(keep, ctypes.c_void_p)
+    _check(L.load().dsa_paged_sparse_attn(ctypes.byref(a), ctypes.byref(kv.args), _stream(stream)))
+    return out, lse_t
+
+
+def paged_append_rows(src: torch.Tensor, pool: torch.Tensor, kv: PagedKV, stream=None):
+    """dsa_paged_append_rows: src [B, ...] (one row per request) goes to each
+    request's last position, seq_lens[b] - 1, of pool [num_pages, page_size, ...]."""
+    _need(src, "src")
+    _need(pool, "pool", dtype=src.dtype)
+    B = src.shape[0]
+    if B != kv.B:
+        raise ValueError("src must have one row per request")
+    kv.check_pool(pool, "pool", tuple(src.shape[1:]))
+    row_bytes = (src.numel() // B) * src.element_size()
+    _check(L.load().dsa_paged_append_rows(_ptr(src), B, row_bytes, _ptr(pool), ctypes.byref(kv.args),
+                                          _stream(stream)))
+
+
 def quantize_fp8_rows(x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
                       scale: Optional[torch.Tensor] = None, stream=None):
     """Per-token fp8 quantisation (dsa_quantize_fp8_rows): x is bf16 with the
@@ -281,11 +411,23 @@ class LayerStack:
 
     def __init__(self, layers: List[dict], topk: int, *, scale: float = 0.0,
                  pos_offset: Optional[int] = None, lse: bool = False, shared_out: bool = False,
-                 events: bool = False):
+                 events: bool = False, kv: Optional[PagedKV] = None):
+        """kv: a PagedKV for one decode step over paged caches (every layer's
+        k_idx, k_scale, k and v are then page pools and n_q must be 1)."""
         l0 = layers[0]
         B, n_q, H_I, D_I = l0["q_idx"].shape
-        n_k = l0["k_idx"].shape[1]
+        n_k = l0["k_idx"].shape[1] if kv is None else kv.max_seq_len
         _, _, H, D = l0["q"].shape
+        if kv is not None:
+            if n_q != 1:
+                raise ValueError("a paged stack is one decode step: n_q must be 1")
+            for i, ly in enumerate(layers):
+                kv.check_pool(ly["k_idx"], f"layers[{i}].k_idx", (D_I,))
+                kv.check_pool(ly["k"], f"layers[{i}].k", (D,))
+                kv.check_pool(ly["v"], f"layers[{i}].v", (D,))
+                if ly.get("k_scale") is not None:
+                    kv.check_pool(ly["k_scale"], f"layers[{i}].k_scale", ())
+        self.kv = kv
         if pos_offset is None:
             pos_offset = n_k - n_q
         code = _dtype_code(l0["q_idx"])
@@ -341,7 +483,11 @@ class LayerStack:
 
     def run(self, pattern: Optional[str] = None, freq: int = 0, stream=None):
         pat = None if pattern is None else pattern.encode()
-        _check(L.load().dsa_layer_stack_run(ctypes.byref(self.args), pat, int(freq), _stream(stream)))
+        if self.kv is None:
+            _check(L.load().dsa_layer_stack_run(ctypes.byref(self.args), pat, int(freq), _stream(stream)))
+        else:
+            _check(L.load().dsa_paged_layer_stack_run(ctypes.byref(self.args), ctypes.byref(self.kv.args), pat,
+                                                      int(freq), _stream(stream)))
         return self.idx_buf, self.outs, self.lses
 
     def layer_times_ms(self) -> List[float]:

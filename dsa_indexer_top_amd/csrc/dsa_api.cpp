@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "dsa.h"
@@ -198,8 +199,9 @@ size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk) {
   sz += round_up(rows * C * 4, 256);  // cand_key
   sz += round_up(rows * C * 4, 256);  // cand_idx
   if (n_q == 1) {
-    sz += round_up((size_t)B * n_k * 4, 256);  // decode keys
-    sz += (size_t)B * kDecodeHistBins * 4;     // decode histogram (a multiple of 256 B) ...
+    sz += round_up((size_t)B * n_k * 4, 256);                        // decode keys
+    sz += round_up(((size_t)B + kDecodeTargetBlocks) * 3 * 4, 256);  // ragged-decode block plan
+    sz += (size_t)B * kDecodeHistBins * 4;  // decode histogram (a multiple of 256 B) ...
   }
   sz += round_up(rows * 4, 256);  // ... directly followed by cand_cnt
   return sz;
@@ -216,6 +218,8 @@ void indexer_bind_workspace(IndexerParams& p, void* ws) {
   if (p.n_q == 1) {
     p.dec_keys = (uint32_t*)c;
     c += round_up((size_t)p.B * p.n_k * 4, 256);
+    p.dec_work = (int32_t*)c;
+    c += round_up(((size_t)p.B + kDecodeTargetBlocks) * 3 * 4, 256);
     p.dec_hist = (uint32_t*)c;
     c += (size_t)p.B * kDecodeHistBins * 4;
   }
@@ -381,8 +385,8 @@ dsa_status dsa_quantize_fp8_rows(const void* x, int64_t rows, int32_t cols, void
   return ok();
 }
 
-dsa_status dsa_layer_stack_run(const dsa_stack_args* a, const char* pattern, int32_t freq, void* stream) {
-  const char* what = "layer_stack_run";
+static dsa_status stack_run(const dsa_stack_args* a, const dsa::PagedKV* kv, const char* pattern, int32_t freq,
+                            void* stream, const char* what) {
   dsa_status st = check_stack_shape(a, what);
   if (st != DSA_OK) return st;
   const int n = a->n_layers;
@@ -416,15 +420,17 @@ dsa_status dsa_layer_stack_run(const dsa_stack_args* a, const char* pattern, int
     }
     if (P[(size_t)l] == 'F') {
       // F layer: compute fresh indices and overwrite the single cached buffer
-      const dsa::IndexerParams ip = make_indexer_params(&a->indexer, a->q_idx[l], a->k_idx[l], a->w[l],
-                                                        fp8 ? a->q_scale[l] : nullptr, fp8 ? a->k_scale[l] : nullptr,
-                                                        a->idx_buf, nullptr, nullptr, a->workspace);
+      dsa::IndexerParams ip = make_indexer_params(&a->indexer, a->q_idx[l], a->k_idx[l], a->w[l],
+                                                  fp8 ? a->q_scale[l] : nullptr, fp8 ? a->k_scale[l] : nullptr,
+                                                  a->idx_buf, nullptr, nullptr, a->workspace);
+      if (kv) ip.kv = *kv;
       st = run_indexer(ip, s);
       if (st != DSA_OK) return st;
     }
     // every layer: sparse attention over the cached indices
-    const dsa::AttnParams ap = make_attn_params(&a->attn, a->q[l], a->k[l], a->v[l], a->idx_buf, a->out[l],
-                                                a->lse ? a->lse[l] : nullptr, a->workspace);
+    dsa::AttnParams ap = make_attn_params(&a->attn, a->q[l], a->k[l], a->v[l], a->idx_buf, a->out[l],
+                                          a->lse ? a->lse[l] : nullptr, a->workspace);
+    if (kv) ap.kv = *kv;
     st = run_attn(ap, s);
     if (st != DSA_OK) return st;
   }
@@ -432,6 +438,110 @@ dsa_status dsa_layer_stack_run(const dsa_stack_args* a, const char* pattern, int
     const hipError_t e = hipEventRecord((hipEvent_t)a->layer_events[n], s);
     if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipEventRecord: %s", what, hipGetErrorString(e));
   }
+  return ok();
+}
+
+dsa_status dsa_layer_stack_run(const dsa_stack_args* a, const char* pattern, int32_t freq, void* stream) {
+  return stack_run(a, nullptr, pattern, freq, stream, "layer_stack_run");
+}
+
+// Validates the paged layout for decode shapes (n_q == 1, n_k == max_seq_len)
+// and fills the kernels' view of it.
+static dsa_status check_paged(const dsa_paged_kv* kv, int B, int n_q, int n_k, int64_t row_bytes, const char* what,
+                              dsa::PagedKV* out) {
+  if (!kv) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: kv is NULL", what);
+  if (kv->struct_size != sizeof(dsa_paged_kv))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: kv struct_size %u != %zu", what, kv->struct_size, sizeof(dsa_paged_kv));
+  if (n_q != 1) return fail(DSA_ERR_UNSUPPORTED, "%s: paged calls are decode only (n_q must be 1, got %d)", what, n_q);
+  if (kv->max_seq_len < 1 || n_k != kv->max_seq_len)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: n_k (%d) must equal kv->max_seq_len (%d) >= 1", what, n_k,
+                kv->max_seq_len);
+  if (kv->page_size < 32 || kv->page_size % 32 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: page_size=%d must be a positive multiple of 32", what, kv->page_size);
+  if (kv->max_pages < 1 || kv->num_pages < 1)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: max_pages and num_pages must be >= 1", what);
+  if ((int64_t)kv->max_pages * kv->page_size < kv->max_seq_len)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: max_pages * page_size < max_seq_len", what);
+  int64_t n;
+  if ((int64_t)kv->num_pages * kv->page_size > INT32_MAX ||
+      !count4(kv->num_pages, kv->page_size, row_bytes, 1, &n) || !count4(B, kv->max_pages, 1, 1, &n))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: pool or block table sizes overflow", what);
+  if (!kv->seq_lens || !kv->block_table || !aligned(kv->seq_lens, 4) || !aligned(kv->block_table, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: seq_lens and block_table are required (4-byte aligned)", what);
+  out->seq_lens = kv->seq_lens;
+  out->block_table = kv->block_table;
+  out->page_size = kv->page_size;
+  out->max_pages = kv->max_pages;
+  out->num_pages = kv->num_pages;
+  return DSA_OK;
+}
+
+dsa_status dsa_paged_indexer_topk(const dsa_indexer_args* a, const dsa_paged_kv* kv, void* stream) {
+  const char* what = "paged_indexer_topk";
+  dsa_status st = check_indexer_shape(a, what);
+  if (st != DSA_OK) return st;
+  dsa::PagedKV pk;
+  st = check_paged(kv, a->B, a->n_q, a->n_k, (int64_t)a->head_dim * (a->dtype == DSA_FP8_E4M3FN ? 1 : 2), what, &pk);
+  if (st != DSA_OK) return st;
+  st = check_indexer_ptrs(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx, what);
+  if (st != DSA_OK) return st;
+  if ((a->out_scores && !aligned(a->out_scores, 4)) || (a->debug_full_scores && !aligned(a->debug_full_scores, 4)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: misaligned out_scores/debug_full_scores", what);
+  const size_t need = dsa::indexer_workspace_bytes(a->B, a->n_q, a->n_k, a->topk);
+  st = check_workspace(a->workspace, a->workspace_bytes, need, what);
+  if (st != DSA_OK) return st;
+  dsa::IndexerParams p = make_indexer_params(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx,
+                                             a->out_scores, a->debug_full_scores, a->workspace);
+  p.kv = pk;
+  p.ev = a->phase_events;
+  st = run_indexer(p, (hipStream_t)stream);
+  return st == DSA_OK ? ok() : st;
+}
+
+dsa_status dsa_paged_sparse_attn(const dsa_attn_args* a, const dsa_paged_kv* kv, void* stream) {
+  const char* what = "paged_sparse_attn";
+  dsa_status st = check_attn_shape(a, what);
+  if (st != DSA_OK) return st;
+  dsa::PagedKV pk;
+  st = check_paged(kv, a->B, a->n_q, a->n_k, (int64_t)a->head_dim * 2, what, &pk);
+  if (st != DSA_OK) return st;
+  st = check_attn_ptrs(a->q, a->k, a->v, a->idx, a->out, a->lse, what);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa::attn_workspace_bytes(a->B, a->n_q, a->n_k, a->n_heads, a->head_dim, a->topk);
+  st = check_workspace(a->workspace, a->workspace_bytes, need, what);
+  if (st != DSA_OK) return st;
+  dsa::AttnParams p = make_attn_params(a, a->q, a->k, a->v, a->idx, a->out, a->lse, a->workspace);
+  p.kv = pk;
+  p.ev = a->phase_events;
+  st = run_attn(p, (hipStream_t)stream);
+  return st == DSA_OK ? ok() : st;
+}
+
+dsa_status dsa_paged_layer_stack_run(const dsa_stack_args* a, const dsa_paged_kv* kv, const char* pattern,
+                                     int32_t freq, void* stream) {
+  const char* what = "paged_layer_stack_run";
+  dsa_status st = check_stack_shape(a, what);
+  if (st != DSA_OK) return st;
+  dsa::PagedKV pk;
+  const int64_t rb = std::max<int64_t>((int64_t)a->indexer.head_dim * 2, (int64_t)a->attn.head_dim * 2);
+  st = check_paged(kv, a->indexer.B, a->indexer.n_q, a->indexer.n_k, rb, what, &pk);
+  if (st != DSA_OK) return st;
+  return stack_run(a, &pk, pattern, freq, stream, what);
+}
+
+dsa_status dsa_paged_append_rows(const void* src, int32_t B, int32_t row_bytes, void* pool, const dsa_paged_kv* kv,
+                                 void* stream) {
+  const char* what = "paged_append_rows";
+  if (B < 1 || B > kMaxB) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: B=%d out of 1..%d", what, B, kMaxB);
+  if (row_bytes < 4 || row_bytes % 4 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: row_bytes=%d must be a positive multiple of 4", what, row_bytes);
+  dsa::PagedKV pk;
+  dsa_status st = check_paged(kv, B, 1, kv ? kv->max_seq_len : 0, row_bytes, what, &pk);
+  if (st != DSA_OK) return st;
+  if (!src || !pool || !aligned(src, 4) || !aligned(pool, 4))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: src and pool are required (4-byte aligned)", what);
+  const hipError_t e = dsa::launch_paged_append_rows(src, B, row_bytes, pool, pk, kv->max_seq_len, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
   return ok();
 }
 

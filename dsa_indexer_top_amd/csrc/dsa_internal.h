@@ -27,6 +27,32 @@ constexpr int kDecodeHistBins = 1 << kDecodeHistBits;
 constexpr int kDecodeWaveKeys = 32;          // keys per wave step of the score kernel
 constexpr int kDecodeBlockKeys = 4 * kDecodeWaveKeys;
 constexpr int kDecodeCollectKeys = 4096;     // keys per block of the collect kernel
+constexpr int kDecodeTargetBlocks = 512;     // score blocks per decode call (two per CU)
+
+// Paged, ragged decode: token s of request b is row
+// block_table[b * max_pages + s / page_size] * page_size + s % page_size of the
+// pools; request b has seq_lens[b] tokens. block_table == nullptr: flat layout.
+struct PagedKV {
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int page_size, max_pages, num_pages;
+};
+
+// Decode context length of request b (clamped to [0, n_k]), or the flat one.
+__device__ __forceinline__ int decode_len(const PagedKV& kv, int b, int pos_offset, int n_k) {
+  if (kv.seq_lens) {
+    const int s = kv.seq_lens[b];
+    return s < 0 ? 0 : (s > n_k ? n_k : s);
+  }
+  return min(pos_offset + 1, n_k);
+}
+
+// Pool row of token s of request b (page id clamped into the pool).
+__device__ __forceinline__ size_t paged_row(const PagedKV& kv, int b, int s) {
+  int page = kv.block_table[(size_t)b * kv.max_pages + s / kv.page_size];
+  page = page < 0 ? 0 : (page >= kv.num_pages ? kv.num_pages - 1 : page);
+  return (size_t)page * kv.page_size + s % kv.page_size;
+}
 
 struct IndexerParams {
   int B, n_q, n_k, pos_offset, H, D, topk, fp8;
@@ -45,6 +71,9 @@ struct IndexerParams {
   int C;
   uint32_t* dec_keys;   // decode: [B, n_k] score keys
   uint32_t* dec_hist;   // decode: [B, kDecodeHistBins], directly followed by cand_cnt
+  int32_t* dec_work;    // decode: [B + kDecodeTargetBlocks, 3] (request, k0, k1) per score
+                        // block, planned on the device when lengths are ragged (kv.seq_lens)
+  PagedKV kv;           // decode only: paged pools (kv.block_table) or flat
   void* const* ev;      // optional phase events (3): before scores, after scores, after select
 };
 
@@ -64,6 +93,7 @@ struct AttnParams {
   float* lse;
   int nsplit;           // >1: split-K over the idx list (decode), partials in ws
   float* part;          // [rows, nsplit, H, kAttnPartStride]: O[D], max, sum, pad
+  PagedKV kv;           // decode only: paged pools (kv.block_table) or flat
   void* const* ev;      // optional phase events (2): before, after
 };
 
@@ -83,6 +113,8 @@ void indexer_bind_workspace(IndexerParams& p, void* ws);
 hipError_t launch_indexer_prefill(const IndexerParams& p, hipStream_t s);
 hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_paged_append_rows(const void* src, int B, int row_bytes, void* pool, const PagedKV& kv,
+                                    int max_seq_len, hipStream_t s);
 hipError_t launch_quantize_fp8_rows(const void* x, int64_t rows, int cols, void* out, float* scale, hipStream_t s);
 
 }  // namespace dsa

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void sparse_attn_kernel(AttnPar
   const int split = wid - row * ns;
   const int b = row / p.n_q;
   const int t = row - b * p.n_q;
-  const int pos = p.pos_offset + t;
+  const bool paged = p.kv.block_table != nullptr;  // decode over page pools (n_q == 1)
+  const int pos = p.kv.seq_lens ? decode_len(p.kv, b, 0, p.n_k) - 1 : p.pos_offset + t;
   const int per = ((p.topk + ns - 1) / ns + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
   const int e0 = split * per;
   const int e1 = min(e0 + per, p.topk);
@@ -84,8 +85,8 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void sparse_attn_kernel(AttnPar
       qb[ks] = v;
     }
   }
-  const unsigned char* kb = (const unsigned char*)p.k + (size_t)b * p.n_k * D * 2;
-  const unsigned char* vb = (const unsigned char*)p.v + (size_t)b * p.n_k * D * 2;
+  const unsigned char* kb = (const unsigned char*)p.k + (paged ? 0 : (size_t)b * p.n_k * D * 2);
+  const unsigned char* vb = (const unsigned char*)p.v + (paged ? 0 : (size_t)b * p.n_k * D * 2);
   const int32_t* irow = p.idx + (size_t)row * p.topk;
   unsigned char* vl = lds_v[wave];
   const int vr = lane / S::LPR, vc = lane % S::LPR;  // V load: row in group, 16-byte column
@@ -103,7 +104,9 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void sparse_attn_kernel(AttnPar
       raw_next = e < e1 ? irow[e] : -1;
     }
     const bool valid = raw >= 0 && raw <= pos && raw < p.n_k;
-    const int key = valid ? raw : 0;
+    // K/V row of this entry: the token itself, or its pool row under paging
+    // (an invalid entry reads row 0 of the request, or of the pool; its weight is 0)
+    const int key = !valid ? 0 : (paged ? (int)paged_row(p.kv, b, raw) : raw);
     const uint32_t vmask = (uint32_t)ballot(valid);  // bit j: entry c0 + j is valid
 
     // gathers: K rows as A fragments, V rows into registers

@@ -242,6 +242,7 @@ struct FinalizeParams {
   const int32_t* cand_idx;
   const int32_t* cand_cnt;
   const uint32_t* full_keys;  // decode: [rows, n_k] keys for the overflow path
+  PagedKV kv;                 // decode: per-request lengths (kv.seq_lens) or none
   int32_t* out_idx;
   float* out_scores;
 };
@@ -326,9 +327,8 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
   __shared__ uint32_t hist[256];
   __shared__ int scratch[17];
   __shared__ int sh_n;
-  const int r = blockIdx.x;
-  const int t = r % p.n_q;
-  const int n_valid = min(p.pos_offset + t + 1, p.n_k);
+  const int r = blockIdx.x;  // n_q == 1: row = request
+  const int n_valid = decode_len(p.kv, r, p.pos_offset, p.n_k);
   const int k_eff = min(p.topk, n_valid);
   const int cnt = p.cand_cnt[r];
   if (cnt <= p.C) {
@@ -393,6 +393,7 @@ hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s
   p.cand_idx = ip.cand_idx;
   p.cand_cnt = ip.cand_cnt;
   p.full_keys = ip.dec_keys;
+  p.kv = ip.kv;
   p.out_idx = ip.out_idx;
   p.out_scores = ip.out_scores;
   if (ip.n_q == 1)
@@ -404,10 +405,49 @@ hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s
 
 // ---------------------------------------------------------------- decode path
 
-__global__ void fill_u32_kernel(uint32_t* __restrict__ a, size_t n, uint32_t v) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    a[i] = v;
+// Decode set-up: zeroes the histograms and candidate counters (n words from
+// p.dec_hist, every block) and, for ragged lengths, block 0 plans the score
+// kernel's blocks: request b's keys are cut into 128-key units and each block
+// takes up to per = ceil(U / aim) units of one request (U = all requests'
+// units, aim = max(target - B, target / 2)). Block j gets (request, k0, k1) in
+// dec_work[j]; entries past the last planned block get request -1. The block
+// count is at most aim + B <= target + B, since
+// sum_b ceil(u_b / per) <= U / per + B.
+__global__ __launch_bounds__(256) void decode_prepare_kernel(IndexerParams p, size_t n, int n_work) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p.dec_hist[i] = 0u;
+  if (blockIdx.x != 0 || !p.kv.seq_lens) return;
+  __shared__ int scratch[17];
+  __shared__ unsigned long long sh_units;
+  const int per_thread = (p.B + (int)blockDim.x - 1) / (int)blockDim.x;  // requests b0 .. b0 + per_thread - 1
+  const int b0 = (int)threadIdx.x * per_thread, b1 = min(b0 + per_thread, p.B);
+  if (threadIdx.x == 0) sh_units = 0ull;
+  __syncthreads();
+  unsigned long long units = 0ull;
+  for (int b = b0; b < b1; ++b)
+    units += (unsigned long long)((decode_len(p.kv, b, 0, p.n_k) + kDecodeBlockKeys - 1) / kDecodeBlockKeys);
+  atomicAdd(&sh_units, units);
+  __syncthreads();
+  const unsigned long long U = sh_units;
+  // aim at target - B blocks so that the rounding up per request still leaves
+  // at most target blocks: one even round of two blocks per CU, no tail
+  const unsigned long long aim = (unsigned long long)max(kDecodeTargetBlocks - p.B, kDecodeTargetBlocks / 2);
+  const long long per = U == 0ull ? 1ll : (long long)((U + aim - 1) / aim);
+  const long long span = per * kDecodeBlockKeys;  // keys per planned block
+  int nblk = 0;
+  for (int b = b0; b < b1; ++b) nblk += (int)((decode_len(p.kv, b, 0, p.n_k) + span - 1) / span);
+  int total;
+  int at = block_excl_scan(nblk, scratch, &total);
+  for (int b = b0; b < b1; ++b) {
+    const int len = decode_len(p.kv, b, 0, p.n_k);
+    for (long long k = 0; k < len; k += span, ++at) {
+      int32_t* wk = p.dec_work + 3 * (size_t)at;
+      wk[0] = b;
+      wk[1] = (int)k;
+      wk[2] = (int)min((long long)len, k + span);
+    }
+  }
+  for (int j = total + (int)threadIdx.x; j < n_work; j += blockDim.x) p.dec_work[3 * (size_t)j] = -1;
 }
 
 // One decode query (up to 64 heads) per request against its key cache. The
@@ -440,14 +480,25 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
   __shared__ uint32_t hist[kDecodeHistBins];
   __shared__ __attribute__((aligned(16))) unsigned char tile[4][T::BYTES];
   const int lane = lane_id(), wave = uniform_i(threadIdx.x >> 6);
-  const int b = blockIdx.y;
+  int b, k0, k1;
+  if (p.kv.seq_lens) {
+    // ragged lengths: this block's (request, key range) from the device-side plan
+    const int32_t* wk = p.dec_work + 3 * (size_t)blockIdx.x;
+    b = uniform_i(wk[0]);
+    if (b < 0) return;  // whole block: past the planned blocks
+    k0 = uniform_i(wk[1]);
+    k1 = uniform_i(wk[2]);
+  } else {
+    // one length for all: gridDim.x blocks split each request's keys evenly
+    b = blockIdx.y;
+    const int kend = decode_len(p.kv, b, p.pos_offset, p.n_k);
+    const int per = ((kend + (int)gridDim.x - 1) / (int)gridDim.x + kDecodeBlockKeys - 1) / kDecodeBlockKeys *
+                    kDecodeBlockKeys;
+    k0 = blockIdx.x * per;
+    k1 = min(k0 + per, kend);
+  }
   const int i32 = lane & 31, g = lane >> 5;
   const size_t row = (size_t)b * p.n_q;  // n_q == 1
-  const int kend = min(p.pos_offset + 1, p.n_k);
-  const int per = ((kend + (int)gridDim.x - 1) / (int)gridDim.x + kDecodeBlockKeys - 1) / kDecodeBlockKeys *
-                  kDecodeBlockKeys;
-  const int k0 = blockIdx.x * per;
-  const int k1 = min(k0 + per, kend);
 
   for (int i = threadIdx.x; i < kDecodeHistBins; i += blockDim.x) hist[i] = 0u;
 
@@ -484,23 +535,43 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     }
   __syncthreads();  // histogram cleared
 
-  const unsigned char* kbase = (const unsigned char*)p.k + (size_t)b * p.n_k * T::RB;
-  const float* kscale = FP8 ? p.k_scale + (size_t)b * p.n_k : nullptr;
+  const bool paged = p.kv.block_table != nullptr;
+  const unsigned char* kbase = (const unsigned char*)p.k + (paged ? 0 : (size_t)b * p.n_k * T::RB);
+  const float* kscale = FP8 ? p.k_scale + (paged ? 0 : (size_t)b * p.n_k) : nullptr;
   uint32_t* keys_out = p.dec_keys + (size_t)b * p.n_k;
   unsigned char* lt = tile[wave];
   const int lr = lane / T::LPR, lc = lane % T::LPR;  // load: row in group, 16-byte chunk
 
-  // rows base .. base + 31, coalesced (rows past k1 read row 0, masked later)
+  // Paged: the page ids of this wave's steps are held one per lane (lane j:
+  // step pg0 + j) and read with readlane, so a step's row loads never wait on
+  // a block-table load (which would also drain the loads of the step before
+  // it); the table is re-read once per 64 steps.
+  const int wbase = k0 + kDecodeWaveKeys * wave;  // this wave's first step
+  int pg = 0, pg0 = -64;
+  auto pool_row = [&](int base) -> size_t {
+    if (!paged) return (size_t)base;
+    const int i = (base - wbase) / kDecodeBlockKeys;  // wave-uniform step number
+    if (i - pg0 >= 64) {
+      pg0 = i;
+      const int kk = base + kDecodeBlockKeys * lane;
+      int page = kk < k1 ? p.kv.block_table[(size_t)b * p.kv.max_pages + kk / p.kv.page_size] : 0;
+      pg = page < 0 ? 0 : (page >= p.kv.num_pages ? p.kv.num_pages - 1 : page);
+    }
+    const int page = __builtin_amdgcn_readlane(pg, i - pg0);
+    return (size_t)page * p.kv.page_size + base % p.kv.page_size;
+  };
+  // rows base .. base + 31, coalesced; rows past k1 repeat the step's last
+  // valid row (masked later). A step lies inside one page (page_size is a
+  // multiple of 32 and steps start at multiples of 32).
   auto load_step = [&](i32x4 (&buf)[T::NI], float& ksc, int base) {
+    const size_t r0 = pool_row(base);  // pool row of key `base`
+    const int last = k1 - 1 - base;
 #pragma unroll
     for (int i = 0; i < T::NI; ++i) {
-      const int key = base + T::RPI * i + lr;
-      buf[i] = *(const i32x4*)(kbase + (size_t)(key < k1 ? key : 0) * T::RB + 16 * lc);
+      const int kr = min(T::RPI * i + lr, last);
+      buf[i] = *(const i32x4*)(kbase + (r0 + kr) * T::RB + 16 * lc);
     }
-    if constexpr (FP8) {
-      const int key = base + i32;
-      ksc = kscale[key < k1 ? key : 0];
-    }
+    if constexpr (FP8) ksc = kscale[r0 + min(i32, last)];
   };
   // one step: rows to LDS, refill the buffer with the step two ahead, MFMAs
   // on fragments read from LDS, epilogue
@@ -609,8 +680,9 @@ __global__ __launch_bounds__(256) void decode_collect_kernel(IndexerParams p) {
   __shared__ int scratch[17];
   __shared__ int sh_base;
   const int b = blockIdx.y;
-  const int n_valid = min(p.pos_offset + 1, p.n_k);
+  const int n_valid = decode_len(p.kv, b, p.pos_offset, p.n_k);
   const int k_eff = min(p.topk, n_valid);
+  if ((int)blockIdx.x * kDecodeCollectKeys >= n_valid) return;  // uniform: no keys here (or none at all)
   const uint32_t tbin = (uint32_t)block_threshold_bin(p.dec_hist + (size_t)b * kDecodeHistBins, k_eff, scratch);
   const int beg = blockIdx.x * kDecodeCollectKeys, end = min(beg + kDecodeCollectKeys, n_valid);
   const uint32_t* keys = p.dec_keys + (size_t)b * p.n_k;
@@ -645,14 +717,20 @@ __global__ __launch_bounds__(256) void decode_collect_kernel(IndexerParams p) {
   }
 }
 
-template <int D, int MB, bool FP8>
-static void launch_decode_scores_t(const IndexerParams& p, hipStream_t s) {
-  // about 512 blocks in all (two per CU), at least one block step each
+// Score blocks of a decode call: the planned list for ragged lengths, else
+// (blocks per request, B) with about kDecodeTargetBlocks blocks in all, at
+// least one block step each.
+static dim3 decode_score_grid(const IndexerParams& p) {
+  if (p.kv.seq_lens) return dim3(p.B + kDecodeTargetBlocks, 1);
   const int kend = std::min(p.pos_offset + 1, p.n_k);
   const int steps = (kend + kDecodeBlockKeys - 1) / kDecodeBlockKeys;
-  int nb = 512 / p.B;
-  nb = std::max(1, std::min(nb, steps));
-  const dim3 grid(nb, p.B);
+  const int nb = std::max(1, std::min(kDecodeTargetBlocks / p.B, steps));
+  return dim3(nb, p.B);
+}
+
+template <int D, int MB, bool FP8>
+static void launch_decode_scores_t(const IndexerParams& p, hipStream_t s) {
+  const dim3 grid = decode_score_grid(p);
   if (p.dump)
     hipLaunchKernelGGL((indexer_decode_kernel<D, MB, FP8, true>), grid, dim3(256), 0, s, p);
   else
@@ -660,11 +738,11 @@ static void launch_decode_scores_t(const IndexerParams& p, hipStream_t s) {
 }
 
 hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
-  // zero the histograms and the candidate counters that follow them (a fill
-  // kernel, not a memset node)
+  // zero the histograms and the candidate counters that follow them (a
+  // kernel, not a memset node), and plan ragged score blocks
   const size_t nz = (size_t)p.B * kDecodeHistBins + (size_t)p.B;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 1024)), dim3(256), 0, s,
-                     p.dec_hist, nz, 0u);
+  hipLaunchKernelGGL(decode_prepare_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 1024)), dim3(256), 0,
+                     s, p, nz, p.B + kDecodeTargetBlocks);
   hipError_t e = record_phase(p.ev, 0, s);
   if (e != hipSuccess) return e;
   const bool two = p.H > 32;
@@ -680,8 +758,8 @@ hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   e = record_phase(p.ev, 1, s);
   if (e != hipSuccess) return e;
-  const int n_valid = std::min(p.pos_offset + 1, p.n_k);
-  const int ncb = (n_valid + kDecodeCollectKeys - 1) / kDecodeCollectKeys;
+  const int n_max = p.kv.seq_lens ? p.n_k : std::min(p.pos_offset + 1, p.n_k);
+  const int ncb = (n_max + kDecodeCollectKeys - 1) / kDecodeCollectKeys;
   hipLaunchKernelGGL(decode_collect_kernel, dim3(ncb, p.B), dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -166,6 +166,56 @@ def seeded_pattern(n_layers: int, n_full: int, seed: int) -> str:
     return "".join(chars)
 
 
+@dataclass
+class PagedLayout:
+    """A paged, ragged decode cache layout. seq_lens: int32 [B] (may hold values
+    outside [0, max_seq_len] to exercise clamping); block_table: int32
+    [B, max_pages], request b's pages in order, entries it does not use = -1."""
+    seq_lens: torch.Tensor
+    block_table: torch.Tensor
+    page_size: int
+    num_pages: int
+    max_seq_len: int
+
+    def to(self, device) -> "PagedLayout":
+        return PagedLayout(self.seq_lens.to(device), self.block_table.to(device), self.page_size,
+                           self.num_pages, self.max_seq_len)
+
+
+def make_paged_layout(seq_lens, page_size: int, max_seq_len: int, *, seed: int,
+                      spare_pages: int = 3) -> PagedLayout:
+    """Request b gets ceil(min(max(seq_lens[b], 0), max_seq_len) / page_size)
+    pages; all pages of the pool (plus spare_pages nobody uses) are handed out in
+    the order of a seeded permutation, so neighbouring tokens of a request sit
+    in unrelated pages."""
+    lens = [int(x) for x in seq_lens]
+    max_pages = -(-max_seq_len // page_size)
+    need = [-(-min(max(n, 0), max_seq_len) // page_size) for n in lens]
+    num_pages = sum(need) + spare_pages
+    perm = np.random.default_rng(seed).permutation(num_pages)
+    bt = np.full((len(lens), max_pages), -1, dtype=np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[at:at + n]
+        at += n
+    return PagedLayout(torch.tensor(lens, dtype=torch.int32), torch.from_numpy(bt), page_size, num_pages,
+                       max_seq_len)
+
+
+def scatter_to_pages(flat: torch.Tensor, layout: PagedLayout, junk: torch.Tensor) -> torch.Tensor:
+    """Page pool [num_pages, page_size, ...] holding flat[b, s] ([B, max_seq_len,
+    ...]) at request b's token s for every s below its clamped length; every
+    other slot keeps the value of junk (same shape as the pool)."""
+    pool = junk.clone()
+    bt = layout.block_table.cpu()
+    for b in range(flat.shape[0]):
+        n = min(max(int(layout.seq_lens[b]), 0), layout.max_seq_len)
+        for s in range(0, n, layout.page_size):
+            m = min(layout.page_size, n - s)
+            pool[int(bt[b, s // layout.page_size]), :m] = flat[b, s:s + m].to(pool.device)
+    return pool
+
+
 def host_bits(t: Optional[torch.Tensor]):
     """Raw bits of a tensor as a numpy array on the host: bf16 -> uint16,
     float8_e4m3fn -> uint8, fp32 -> float32, int32 -> int32."""

@@ -176,6 +176,32 @@ typedef struct {
   size_t workspace_bytes;
 } dsa_stack_args;
 
+/* Paged, ragged decode: the KV layout a serving engine keeps. One query token
+ * per request; request b's context holds seq_lens[b] tokens, the new token
+ * being the last (position seq_lens[b] - 1), and token s of request b lives
+ * in page block_table[b * max_pages + s / page_size], slot s % page_size, of a
+ * page pool. Pools: indexer keys [num_pages, page_size, head_dim] (indexer
+ * dtype), their fp8 scales [num_pages, page_size] fp32, attention K and V
+ * [num_pages, page_size, head_dim] bf16.
+ *   seq_lens    device int32 [B]; values are clamped to [0, max_seq_len]. A
+ *               request with no tokens gets all -1 indices (attention: out 0,
+ *               lse -inf).
+ *   block_table device int32 [B, max_pages]; the entries of the pages a request
+ *               uses must lie in [0, num_pages). Other entries are not read.
+ *               An out-of-range entry is clamped into the pool: that request's
+ *               results are then unspecified, but no access leaves the pool.
+ *   page_size   a multiple of 32; max_pages * page_size >= max_seq_len.
+ * Indices are logical token positions, so the IndexCache buffer (one index
+ * tensor reused by the S layers, paper listing page, Figure 2 caption) needs
+ * no change under paging. */
+typedef struct {
+  uint32_t struct_size;         /* = sizeof(dsa_paged_kv) */
+  int32_t max_seq_len;          /* host upper bound of seq_lens: sizes grids and workspaces */
+  int32_t page_size, max_pages, num_pages;
+  const int32_t *seq_lens;
+  const int32_t *block_table;
+} dsa_paged_kv;
+
 /* DSA_ABI_VERSION of the built library. */
 int32_t dsa_abi_version(void);
 
@@ -211,6 +237,35 @@ dsa_status dsa_sparse_attn(const dsa_attn_args *args, void *stream);
  * for every layer before anything is enqueued. */
 dsa_status dsa_layer_stack_run(const dsa_stack_args *args, const char *pattern,
                                int32_t index_topk_freq, void *stream);
+
+/* Decode indexer + top-k over a paged, ragged cache. args as for
+ * dsa_indexer_scores_topk with n_q = 1 and n_k = kv->max_seq_len (q_pos_offset
+ * is ignored: request b's query sits at seq_lens[b] - 1); k and k_scale point
+ * at the page pools; debug_full_scores, if given, is [B, max_seq_len] (entries
+ * at or past a request's length are left untouched). out_idx holds logical
+ * token positions. The workspace is dsa_indexer_workspace_size of args. */
+dsa_status dsa_paged_indexer_topk(const dsa_indexer_args *args, const dsa_paged_kv *kv, void *stream);
+
+/* Decode sparse attention over a paged cache. args as for dsa_sparse_attn with
+ * n_q = 1 and n_k = kv->max_seq_len; k and v point at the page pools; idx holds
+ * logical positions (entries < 0 or >= seq_lens[b] are skipped). The workspace
+ * is dsa_attn_workspace_size of args. */
+dsa_status dsa_paged_sparse_attn(const dsa_attn_args *args, const dsa_paged_kv *kv, void *stream);
+
+/* The layer stack of one decode step over paged caches: as
+ * dsa_layer_stack_run with n_q = 1, n_k = kv->max_seq_len, every per-layer
+ * k_idx, k_scale, k and v pointer a page pool (all layers share kv), and
+ * idx_buf [B, topk] holding logical positions. */
+dsa_status dsa_paged_layer_stack_run(const dsa_stack_args *args, const dsa_paged_kv *kv, const char *pattern,
+                                     int32_t index_topk_freq, void *stream);
+
+/* Writes src[b] (row_bytes bytes) to its request's last position
+ * seq_lens[b] - 1 in a page pool [num_pages, page_size, row_bytes]: the step
+ * before the path, run for the new token's indexer key (and fp8 scale), K and
+ * V. Requests with seq_lens[b] < 1 are skipped. row_bytes is a positive
+ * multiple of 4; src and pool are 4-byte aligned device pointers. */
+dsa_status dsa_paged_append_rows(const void *src, int32_t B, int32_t row_bytes, void *pool,
+                                 const dsa_paged_kv *kv, void *stream);
 
 /* Per-token fp8 quantisation of indexer inputs: the step that produces the
  * fp8 e4m3 q_idx / k_idx with per-token fp32 scales that the long-context

@@ -35,6 +35,9 @@ Pinning status (what each function is checked against, besides itself):
                              grids with every midpoint; extremes
   quant.quantize_rows_fp8    the row maximum maps to +-448; dequantisation error
                              within half a step; zero rows
+  paged.*                    the flat functions per request on pools built by
+                             scattering flat rows; junk outside the context;
+                             page renaming; length clamping; append
 No function is "parity unpinned".
 """
 from .formats import bf16_to_f64, e4m3fn_table, e4m3fn_to_f64  # noqa: F401
@@ -49,3 +52,4 @@ from .attention import sparse_attention, sparse_attention_rows  # noqa: F401
 from .pattern import resolve_pattern, PatternError  # noqa: F401
 from .stack import run_stack  # noqa: F401
 from .quant import e4m3fn_encode, quantize_rows_fp8  # noqa: F401
+from . import paged  # noqa: F401

@@ -54,7 +54,8 @@ def _c_layout(tmp_path, struct, fields):
 
 @pytest.mark.parametrize("cls,struct", [(L.IndexerArgs, "dsa_indexer_args"),
                                         (L.AttnArgs, "dsa_attn_args"),
-                                        (L.StackArgs, "dsa_stack_args")])
+                                        (L.StackArgs, "dsa_stack_args"),
+                                        (L.PagedKVArgs, "dsa_paged_kv")])
 def test_ctypes_layout_matches_header(tmp_path, cls, struct):
     fields = [f for f, _ in cls._fields_]
     got = [ctypes.sizeof(cls)] + [getattr(cls, f).offset for f in fields]
@@ -200,3 +201,68 @@ def test_quantize_validation(lib):
     assert q(FAKE + 8, 4, 128, FAKE, FAKE, None) == L.DSA_ERR_INVALID_ARGUMENT  # x not 16-byte aligned
     assert q(FAKE, 4, 128, FAKE + 4, FAKE, None) == L.DSA_ERR_INVALID_ARGUMENT  # out not 8-byte aligned
     assert q(FAKE, 0, 128, None, None, None) == L.DSA_OK                        # nothing to do, no launch
+
+
+def _kv(**kw):
+    kv = L.PagedKVArgs()
+    kv.struct_size = ctypes.sizeof(L.PagedKVArgs)
+    kv.max_seq_len, kv.page_size, kv.max_pages, kv.num_pages = 256, 64, 4, 16
+    kv.seq_lens = kv.block_table = FAKE
+    for k, v in kw.items():
+        setattr(kv, k, v)
+    return kv
+
+
+@pytest.mark.parametrize("kvmut,amut,status", [
+    (dict(struct_size=4), None, L.DSA_ERR_INVALID_ARGUMENT),
+    (dict(page_size=48), None, L.DSA_ERR_UNSUPPORTED),                 # not a multiple of 32
+    (dict(page_size=0), None, L.DSA_ERR_UNSUPPORTED),
+    (dict(max_pages=3), None, L.DSA_ERR_INVALID_ARGUMENT),             # 3 * 64 < max_seq_len
+    (dict(num_pages=0), None, L.DSA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=2 ** 30), None, L.DSA_ERR_INVALID_ARGUMENT),       # pool rows overflow int32
+    (dict(max_seq_len=300), None, L.DSA_ERR_INVALID_ARGUMENT),         # n_k != max_seq_len
+    (dict(seq_lens=None), None, L.DSA_ERR_INVALID_ARGUMENT),
+    (dict(block_table=FAKE + 2), None, L.DSA_ERR_INVALID_ARGUMENT),    # misaligned
+    (dict(), lambda a: (setattr(a, "n_q", 2), setattr(a, "q_pos_offset", 254)), L.DSA_ERR_UNSUPPORTED),
+    (dict(), None, L.DSA_ERR_WORKSPACE),                                # valid layout, no workspace
+])
+def test_paged_validation(lib, kvmut, amut, status):
+    kv = _kv(**kvmut)
+    a = _idx_args(B=2, n_q=1, n_k=256, pos_offset=255, topk=64)
+    if amut:
+        amut(a)
+    assert lib.dsa_paged_indexer_topk(ctypes.byref(a), ctypes.byref(kv), None) == status
+    assert lib.dsa_last_error() != b""
+    at = attn_args(2, 1, 256, 255, 16, 128, 64, 0.0)
+    at.q = at.k = at.v = at.idx = at.out = FAKE
+    if amut:
+        amut(at)
+    assert lib.dsa_paged_sparse_attn(ctypes.byref(at), ctypes.byref(kv), None) == (
+        L.DSA_ERR_WORKSPACE if status == L.DSA_ERR_WORKSPACE else status)
+    assert lib.dsa_paged_indexer_topk(ctypes.byref(a), None, None) == L.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_paged_append_validation(lib):
+    ap = lib.dsa_paged_append_rows
+    kv = _kv()
+    assert ap(FAKE, 0, 256, FAKE, ctypes.byref(kv), None) == L.DSA_ERR_INVALID_ARGUMENT
+    assert ap(FAKE, 2, 6, FAKE, ctypes.byref(kv), None) == L.DSA_ERR_UNSUPPORTED     # not a multiple of 4
+    assert ap(None, 2, 256, FAKE, ctypes.byref(kv), None) == L.DSA_ERR_INVALID_ARGUMENT
+    assert ap(FAKE, 2, 256, FAKE + 2, ctypes.byref(kv), None) == L.DSA_ERR_INVALID_ARGUMENT
+    assert ap(FAKE, 2, 256, FAKE, None, None) == L.DSA_ERR_INVALID_ARGUMENT
+    bad = _kv(page_size=16)
+    assert ap(FAKE, 2, 256, FAKE, ctypes.byref(bad), None) == L.DSA_ERR_UNSUPPORTED
+
+
+def test_paged_stack_validation(lib):
+    a = L.StackArgs()
+    a.struct_size = ctypes.sizeof(L.StackArgs)
+    a.n_layers = 2
+    a.indexer = indexer_args(2, 1, 256, 255, 4, 32, 16, L.DSA_BF16)
+    a.attn = attn_args(2, 1, 256, 255, 4, 64, 16, 0.0)
+    kv = _kv()
+    assert lib.dsa_paged_layer_stack_run(ctypes.byref(a), ctypes.byref(kv), b"SF", 0, None) == L.DSA_ERR_BAD_PATTERN
+    assert lib.dsa_paged_layer_stack_run(ctypes.byref(a), None, b"FS", 0, None) == L.DSA_ERR_INVALID_ARGUMENT
+    # layout fine, per-layer arrays missing
+    assert lib.dsa_paged_layer_stack_run(ctypes.byref(a), ctypes.byref(kv), b"FS", 0, None) == \
+        L.DSA_ERR_INVALID_ARGUMENT
