@@ -199,9 +199,9 @@ size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk) {
   sz += round_up(rows * C * 4, 256);  // cand_key
   sz += round_up(rows * C * 4, 256);  // cand_idx
   if (n_q == 1) {
-    sz += round_up((size_t)B * n_k * 4, 256);                        // decode keys
+    sz += (size_t)B * decode_key_stride(n_k) * 4;                    // decode keys
     sz += round_up(((size_t)B + kDecodeTargetBlocks) * 3 * 4, 256);  // ragged-decode block plan
-    sz += (size_t)B * kDecodeHistBins * 4;  // decode histogram (a multiple of 256 B) ...
+    sz += (size_t)B * kDecodeHistStride * 4;  // decode histograms (a multiple of 256 B) ...
   }
   sz += round_up(rows * 4, 256);  // ... directly followed by cand_cnt
   return sz;
@@ -217,11 +217,11 @@ void indexer_bind_workspace(IndexerParams& p, void* ws) {
   c += round_up(rows * p.C * 4, 256);
   if (p.n_q == 1) {
     p.dec_keys = (uint32_t*)c;
-    c += round_up((size_t)p.B * p.n_k * 4, 256);
+    c += (size_t)p.B * decode_key_stride(p.n_k) * 4;
     p.dec_work = (int32_t*)c;
     c += round_up(((size_t)p.B + kDecodeTargetBlocks) * 3 * 4, 256);
     p.dec_hist = (uint32_t*)c;
-    c += (size_t)p.B * kDecodeHistBins * 4;
+    c += (size_t)p.B * kDecodeHistStride * 4;
   }
   p.cand_cnt = (int32_t*)c;
 }

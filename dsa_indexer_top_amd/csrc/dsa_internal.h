@@ -24,6 +24,11 @@ inline int cand_capacity(int topk, bool decode) {
 // Decode path: bins of the first-level histogram of the 32-bit score keys.
 constexpr int kDecodeHistBits = 12;
 constexpr int kDecodeHistBins = 1 << kDecodeHistBits;
+constexpr int kDecodeCoarseBins = 64;  // sums of 64 consecutive bins, stored after them
+constexpr int kDecodeHistStride = kDecodeHistBins + kDecodeCoarseBins;
+// Row stride of the decode score keys: n_k rounded up to 64 keys (256 B), so
+// every row starts aligned and 16-key vector reads stay inside it.
+__host__ __device__ inline size_t decode_key_stride(int n_k) { return ((size_t)n_k + 63) / 64 * 64; }
 constexpr int kDecodeWaveKeys = 32;          // keys per wave step of the score kernel
 constexpr int kDecodeBlockKeys = 4 * kDecodeWaveKeys;
 constexpr int kDecodeCollectKeys = 4096;     // keys per block of the collect kernel
@@ -69,8 +74,9 @@ struct IndexerParams {
   int32_t* cand_idx;    // [rows, C]
   int32_t* cand_cnt;    // [rows]
   int C;
-  uint32_t* dec_keys;   // decode: [B, n_k] score keys
-  uint32_t* dec_hist;   // decode: [B, kDecodeHistBins], directly followed by cand_cnt
+  uint32_t* dec_keys;   // decode: [B, dec_stride] score keys
+  uint32_t* dec_hist;   // decode: [B, kDecodeHistStride] (fine bins, then coarse bins),
+                        // directly followed by cand_cnt (one fill zeroes both)
   int32_t* dec_work;    // decode: [B + kDecodeTargetBlocks, 3] (request, k0, k1) per score
                         // block, planned on the device when lengths are ragged (kv.seq_lens)
   PagedKV kv;           // decode only: paged pools (kv.block_table) or flat

@@ -231,16 +231,24 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void sparse_attn_kernel(AttnPar
 // Merges the split partials of one (query, head) per wave:
 // M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s o_s 2^(m_s - M) / L
 // (m in log2 units; splits with no valid entry have m = -inf, l = 0, o = 0).
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   constexpr int DPL = D / kWave;  // output dims per lane
   const int lane = lane_id();
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int row = blockIdx.y;
   if (h >= p.H) return;
-  const int ns = p.nsplit;  // <= 64
+  const int ns = p.nsplit;  // <= NS <= 64
   const size_t sstride = (size_t)p.H * kAttnPartStride<D>;
   const float* base = p.part + ((size_t)row * ns * p.H + h) * kAttnPartStride<D>;
+  // every split's partial O first (independent of the weights), then m and l,
+  // so all loads are in flight together
+  const float* src = base + DPL * lane;
+  float v[NS][DPL];
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) v[j][c] = j < ns ? src[j * sstride + c] : 0.0f;
   const float ms = lane < ns ? base[lane * sstride + D] : -__builtin_inff();
   const float ls = lane < ns ? base[lane * sstride + D + 1] : 0.0f;
   float M = ms;
@@ -253,21 +261,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   float o[DPL];
 #pragma unroll
   for (int c = 0; c < DPL; ++c) o[c] = 0.0f;
-  const float* src = base + DPL * lane;
-  // 16 splits per round: all loads of a round are issued before their FMAs
-  for (int s0 = 0; s0 < ns; s0 += 16) {
-    float v[16][DPL];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < NS; ++j) {
+    const float fs = j < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j)) : 0.0f;
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) v[j][c] = s0 + j < ns ? src[(s0 + j) * sstride + c] : 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int sp = s0 + j < ns ? s0 + j : 0;
-      const float fs = s0 + j < ns ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), sp)) : 0.0f;
-#pragma unroll
-      for (int c = 0; c < DPL; ++c) o[c] = __builtin_fmaf(fs, v[j][c], o[c]);
-    }
+    for (int c = 0; c < DPL; ++c) o[c] = __builtin_fmaf(fs, v[j][c], o[c]);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   __bf16* dst = (__bf16*)p.out + ((size_t)row * p.H + h) * D + DPL * lane;
@@ -286,7 +284,10 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL((sparse_attn_kernel<D, true>), grid, dim3(kAttnWaves * kWave), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((p.H + 3) / 4, rows), dim3(256), 0, s, p);
+    if (p.nsplit <= 32)
+      hipLaunchKernelGGL((attn_combine_kernel<D, 32>), dim3((p.H + 3) / 4, rows), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<D, 64>), dim3((p.H + 3) / 4, rows), dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL((sparse_attn_kernel<D, false>), grid, dim3(kAttnWaves * kWave), 0, s, p);
   }

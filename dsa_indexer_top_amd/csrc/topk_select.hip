@@ -1,9 +1,9 @@
 // Exact per-row top-k finalisation and the decode-path selection kernels.
 //
-// Order used everywhere: the 64-bit composite key (score_key(score) << 32) |
-// ~index, larger = better, i.e. higher score first and, for equal scores,
-// lower index first. Composite keys are unique, so "the first k in composite
-// order" is exactly the top-k with the library's tie rule.
+// Order used everywhere: higher score first and, for equal scores, lower index
+// first (the 32-bit order key score_key(score), then the index ascending).
+// The pairs (key, index) are unique, so "the first k in that order" is exactly
+// the top-k with the library's tie rule.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -12,34 +12,10 @@
 
 namespace dsa {
 
-// Threads per finalize workgroup: a prefill launch has one workgroup per query
-// row and many rows in flight; a decode launch has one per request, so each
-// is made wide to cut its latency (the sort is one barrier per network stage).
+// Threads per finalize workgroup (prefill: one per query row, decode: one per
+// request): the 8 waves of the radix sort below.
 constexpr int kFinNTPrefill = 512;
-constexpr int kFinNTDecode = 1024;
-
-__device__ __forceinline__ uint64_t composite(uint32_t u, int32_t idx) {
-  return ((uint64_t)u << 32) | (uint64_t)(~(uint32_t)idx);
-}
-
-// Descending bitonic sort of s[0..n) (n a power of two) by the whole workgroup.
-__device__ void block_bitonic_desc(uint64_t* s, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) != 0;  // this pair's segment is ascending
-        const uint64_t a = s[lo], c = s[hi];
-        if (up ? (a > c) : (a < c)) {
-          s[lo] = c;
-          s[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
+constexpr int kFinNTDecode = 512;
 
 // Block-wide exclusive prefix sum of one value per thread (blockDim.x <= 1024).
 __device__ int block_excl_scan(int v, int* scratch /* >= 17 ints */, int* total) {
@@ -152,32 +128,30 @@ __device__ void block_ordered_emit(const uint32_t* keys, const int32_t* __restri
   __syncthreads();
 }
 
-// The same, as composite keys in s[0..).
-__device__ void block_ordered_collect(const uint32_t* keys, const int32_t* __restrict__ idx, int n,
-                                      uint32_t theta, int need, uint64_t* s, int* scratch) {
-  block_ordered_emit(keys, idx, n, theta, need, scratch,
-                     [&](int pos, uint32_t u, int32_t ix) { s[pos] = composite(u, ix); });
-}
 
 // Stable LSD radix sort of kSortN (key, index) pairs in LDS by descending key
-// (equal keys keep their order) by a workgroup of kSortWaves waves. Wave w
-// holds positions 256w + 64j + lane (j < 4) of the current order. Each 8-bit
-// pass ranks every element among the equal digits of its wave (lanes matched
-// by 8 ballots, rows in order, a per-wave histogram carrying the rows before),
-// scans the per-(digit, wave) counts in digit-major order and scatters to the
-// other buffer; after the 4 passes the result is back in (ka, ia).
-// hist: 256 * kSortWaves entries.
+// (equal keys keep their order) by a workgroup of kSortWaves waves. With
+// idx_passes = 2 or 4 (even), that many 8-bit passes by ascending index come
+// first, so equal keys end in ascending index order whatever their order was.
+// Wave w holds positions 256w + 64j + lane (j < 4) of the current order. Each
+// 8-bit pass ranks every element among the equal digits of its wave (lanes
+// matched by 8 ballots, rows in order, a per-wave histogram carrying the rows
+// before), scans the per-(digit, wave) counts in digit-major order and
+// scatters to the other buffer; after the even number of passes the result is
+// back in (ka, ia). hist: 256 * kSortWaves entries.
 constexpr int kSortWaves = 8;
 constexpr int kSortN = kSortWaves * 256;
 
 __device__ void block_radix_sort_desc(uint32_t* ka, int32_t* ia, uint32_t* kb, int32_t* ib, uint32_t* hist,
-                                      int* scratch) {
+                                      int* scratch, int idx_passes = 0) {
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
   const uint64_t gt = ~lt & ~(1ull << lane);
   uint32_t* hw = hist + 256 * w;
 #pragma unroll 1
-  for (int shift = 0; shift < 32; shift += 8) {
+  for (int pass = 0; pass < idx_passes + 4; ++pass) {
+    const bool by_idx = pass < idx_passes;
+    const int shift = 8 * (by_idx ? pass : pass - idx_passes);
     uint32_t u[4], d[4];
     int32_t x[4];
     int rank[4];
@@ -186,7 +160,8 @@ __device__ void block_radix_sort_desc(uint32_t* ka, int32_t* ia, uint32_t* kb, i
       const int e = 256 * w + 64 * j + lane;
       u[j] = ka[e];
       x[j] = ia[e];
-      d[j] = (~u[j] >> shift) & 255u;  // ascending ~key = descending key
+      // ascending index; ascending ~key = descending key
+      d[j] = by_idx ? (((uint32_t)x[j] >> shift) & 255u) : ((~u[j] >> shift) & 255u);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) hw[4 * lane + q] = 0u;
@@ -241,29 +216,22 @@ struct FinalizeParams {
   const uint32_t* cand_key;
   const int32_t* cand_idx;
   const int32_t* cand_cnt;
-  const uint32_t* full_keys;  // decode: [rows, n_k] keys for the overflow path
+  const uint32_t* full_keys;  // decode: [rows, decode_key_stride(n_k)] keys for the overflow path
   PagedKV kv;                 // decode: per-request lengths (kv.seq_lens) or none
   int32_t* out_idx;
   float* out_scores;
 };
 
-__device__ void write_sorted(const FinalizeParams& p, int r, const uint64_t* s, int n_sorted) {
+// Writes the first n_sorted sorted pairs of a row, -1 / -inf padded to topk.
+__device__ void write_sorted(const FinalizeParams& p, int r, const uint32_t* wkey, const int32_t* widx,
+                             int n_sorted) {
   int32_t* oi = p.out_idx + (size_t)r * p.topk;
   float* os = p.out_scores ? p.out_scores + (size_t)r * p.topk : nullptr;
   for (int i = threadIdx.x; i < p.topk; i += blockDim.x) {
     const bool v = i < n_sorted;
-    const uint64_t c = v ? s[i] : 0ull;
-    oi[i] = v ? (int32_t)(~(uint32_t)c) : -1;
-    if (os) os[i] = v ? key_score((uint32_t)(c >> 32)) : -__builtin_inff();
+    oi[i] = v ? widx[i] : -1;
+    if (os) os[i] = v ? key_score(wkey[i]) : -__builtin_inff();
   }
-}
-
-__device__ void pad_and_sort(uint64_t* s, int n_items) {
-  int n = 1;
-  while (n < n_items) n <<= 1;
-  for (int i = n_items + threadIdx.x; i < n; i += blockDim.x) s[i] = 0ull;
-  __syncthreads();
-  block_bitonic_desc(s, n);
 }
 
 // Prefill rows: each candidate list (<= kMaxC entries, in index order)
@@ -307,23 +275,23 @@ __global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(Finaliz
   __syncthreads();
   // stable by key: equal keys stay in index order, the tie rule
   block_radix_sort_desc(wkey, widx, skey, (int32_t*)(skey + kSortN), skey + 2 * kSortN, scratch);
-  int32_t* oi = p.out_idx + (size_t)r * p.topk;
-  float* os = p.out_scores ? p.out_scores + (size_t)r * p.topk : nullptr;
-  for (int i = threadIdx.x; i < p.topk; i += blockDim.x) {
-    const bool v = i < take;
-    oi[i] = v ? widx[i] : -1;
-    if (os) os[i] = v ? key_score(wkey[i]) : -__builtin_inff();
-  }
+  write_sorted(p, r, wkey, widx, take);
 }
 
 // Decode requests: the candidate list is unordered (<= C entries, a superset
 // of the top-k). The k-th key theta is found in LDS; if more entries tie at
 // theta than the top-k takes, a second select over their inverted indices
-// keeps the lowest ones. The winners are then sorted. If the list overflowed,
-// the exact top-k is taken from the request's full key row instead.
+// keeps the lowest ones. The winners (in list order) are radix-sorted by key,
+// then each run of equal keys is put in index order (a run longer than 32:
+// the row is sorted again with index passes first). If the list overflowed,
+// the exact top-k is taken from the request's full key row in index order
+// instead, and the stable key sort alone gives the tie rule.
 __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeParams p) {
+  static_assert(kFinNTDecode == kSortWaves * kWave && kSortN >= kMaxTopk, "sort layout");
+  static_assert(kMaxC >= 2 * kSortN + 256 * kSortWaves, "sort scratch must fit in skey");
   __shared__ uint32_t skey[kMaxC];
-  __shared__ uint64_t s[kMaxTopk];
+  __shared__ uint32_t wkey[kSortN];
+  __shared__ int32_t widx[kSortN];
   __shared__ uint32_t hist[256];
   __shared__ int scratch[17];
   __shared__ int sh_n;
@@ -331,15 +299,17 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
   const int n_valid = decode_len(p.kv, r, p.pos_offset, p.n_k);
   const int k_eff = min(p.topk, n_valid);
   const int cnt = p.cand_cnt[r];
+  int take;
+  bool ordered;  // winners already in index order
   if (cnt <= p.C) {
     const uint32_t* ck = p.cand_key + (size_t)r * p.C;
     const int32_t* ci = p.cand_idx + (size_t)r * p.C;
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
     if (threadIdx.x == 0) sh_n = 0;
     __syncthreads();
-    const int take = min(k_eff, cnt);  // cnt >= k_eff by construction
-    uint32_t theta = 0u;               // below every finite score's key: keep all
-    uint32_t cut = 0u;                 // keep ties with ~index >= cut
+    take = min(k_eff, cnt);  // cnt >= k_eff by construction
+    uint32_t theta = 0u;     // below every finite score's key: keep all
+    uint32_t cut = 0u;       // keep ties with ~index >= cut
     if (cnt > take) {
       int need;
       block_kth_key(skey, cnt, take, hist, &theta, &need);
@@ -365,20 +335,62 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
       int base = 0;
       if (lane_id() == 0 && m) base = atomicAdd(&sh_n, popc64(m));
       base = __shfl(base, 0, 64);
-      if (keep) s[base + mbcnt(m)] = composite(u, ix);
+      if (keep) {
+        wkey[base + mbcnt(m)] = u;
+        widx[base + mbcnt(m)] = ix;
+      }
     }
-    __syncthreads();
-    pad_and_sort(s, take);
-    write_sorted(p, r, s, take);
+    ordered = false;
   } else {
-    const uint32_t* keys = p.full_keys + (size_t)r * p.n_k;
+    const uint32_t* keys = p.full_keys + (size_t)r * decode_key_stride(p.n_k);
     uint32_t theta;
     int need;
     block_kth_key(keys, n_valid, k_eff, hist, &theta, &need);
-    block_ordered_collect(keys, nullptr, n_valid, theta, need, s, scratch);
-    pad_and_sort(s, k_eff);
-    write_sorted(p, r, s, k_eff);
+    block_ordered_emit(keys, nullptr, n_valid, theta, need, scratch, [&](int pos, uint32_t u, int32_t ix) {
+      wkey[pos] = u;
+      widx[pos] = ix;
+    });
+    take = k_eff;
+    ordered = true;
   }
+  // padding (key 0, index -1) sorts last
+  for (int i = take + (int)threadIdx.x; i < kSortN; i += blockDim.x) {
+    wkey[i] = 0u;
+    widx[i] = -1;
+  }
+  __syncthreads();
+  uint32_t* kb = skey;
+  int32_t* ib = (int32_t*)(skey + kSortN);
+  uint32_t* sh = skey + 2 * kSortN;
+  block_radix_sort_desc(wkey, widx, kb, ib, sh, scratch);
+  if (!ordered) {
+    // equal keys are adjacent now, in list order: the thread at the start of
+    // a run puts it in index order (insertion sort); a run longer than 32
+    // sends the whole row to a re-sort with index passes first
+    bool long_run = false;
+    for (int i = threadIdx.x; i + 1 < take; i += blockDim.x) {
+      const uint32_t u = wkey[i];
+      if ((i > 0 && wkey[i - 1] == u) || wkey[i + 1] != u) continue;  // not the start of a run
+      int n = 2;
+      while (i + n < take && n <= 32 && wkey[i + n] == u) ++n;
+      if (n > 32) {
+        long_run = true;
+        continue;
+      }
+      for (int a = i + 1; a < i + n; ++a) {
+        const int32_t x = widx[a];
+        int c = a - 1;
+        while (c >= i && widx[c] > x) {
+          widx[c + 1] = widx[c];
+          --c;
+        }
+        widx[c + 1] = x;
+      }
+    }
+    if (__syncthreads_or(long_run))
+      block_radix_sort_desc(wkey, widx, kb, ib, sh, scratch, n_valid <= 65536 ? 2 : 4);
+  }
+  write_sorted(p, r, wkey, widx, take);
 }
 
 hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s) {
@@ -538,7 +550,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
   const bool paged = p.kv.block_table != nullptr;
   const unsigned char* kbase = (const unsigned char*)p.k + (paged ? 0 : (size_t)b * p.n_k * T::RB);
   const float* kscale = FP8 ? p.k_scale + (paged ? 0 : (size_t)b * p.n_k) : nullptr;
-  uint32_t* keys_out = p.dec_keys + (size_t)b * p.n_k;
+  uint32_t* keys_out = p.dec_keys + (size_t)b * decode_key_stride(p.n_k);
   unsigned char* lt = tile[wave];
   const int lr = lane / T::LPR, lc = lane % T::LPR;  // load: row in group, 16-byte chunk
 
@@ -635,41 +647,36 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     step(buf1, ksc1, base + kDecodeBlockKeys);
   }
   __syncthreads();
-  uint32_t* gh = p.dec_hist + (size_t)b * kDecodeHistBins;
+  uint32_t* gh = p.dec_hist + (size_t)b * kDecodeHistStride;
   for (int i = threadIdx.x; i < kDecodeHistBins; i += blockDim.x) {
     const uint32_t c = hist[i];
     if (c) atomicAdd(&gh[i], c);
   }
+  // coarse bins (64 fine bins each): thread t sums 16 fine bins, four threads
+  // make one coarse bin
+  static_assert(kDecodeHistBins == 256 * 16 && kDecodeCoarseBins * 64 == kDecodeHistBins, "histogram layout");
+  uint32_t cs = 0u;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) cs += hist[16 * threadIdx.x + j];
+  cs += __shfl_xor(cs, 1, 64);
+  cs += __shfl_xor(cs, 2, 64);
+  if ((threadIdx.x & 3) == 0 && cs) atomicAdd(&gh[kDecodeHistBins + (threadIdx.x >> 2)], cs);
 }
 
-// Threshold bin of a request's histogram, by the whole (256-thread) block:
-// the largest T with count(bins >= T) >= k_eff.
-__device__ int block_threshold_bin(const uint32_t* __restrict__ gh, int k_eff, int* scratch) {
-  constexpr int PER = kDecodeHistBins / 256;
-  __shared__ int sh_bin;
-  const int top = kDecodeHistBins - 1 - PER * (int)threadIdx.x;  // thread t owns bins top .. top-PER+1
-  uint32_t c[PER];
-  int loc = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    c[j] = gh[top - j];
-    loc += (int)c[j];
-  }
-  int total;
-  const int before = block_excl_scan(loc, scratch, &total);  // keys in higher bins
-  if (before < k_eff && before + loc >= k_eff) {
-    int cum = before;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      cum += (int)c[j];
-      if (cum >= k_eff) {
-        sh_bin = top - j;
-        break;
-      }
-    }
-  }
-  __syncthreads();
-  return sh_bin;
+// Threshold bin of a request's histogram gh (fine bins, then coarse bins) by
+// one wave: the largest T with count(bins >= T) >= k_eff, found in the
+// coarse bins first and then among the 64 fine bins of the coarse bin found.
+__device__ int wave_threshold_bin(const uint32_t* __restrict__ gh, int k_eff) {
+  const int lane = lane_id();
+  const uint32_t c = gh[kDecodeHistBins + kDecodeCoarseBins - 1 - lane];  // lane 0: top coarse bin
+  const uint32_t ci = wave_incl_scan(c);
+  const int L = uniform_i(__builtin_ctzll(ballot(ci >= (uint32_t)k_eff)));
+  const uint32_t above = __shfl(ci - c, L, 64);  // keys in coarse bins above it
+  const int cb = kDecodeCoarseBins - 1 - L;
+  const uint32_t f = gh[64 * cb + 63 - lane];
+  const uint32_t fi = wave_incl_scan(f) + above;
+  const int L2 = uniform_i(__builtin_ctzll(ballot(fi >= (uint32_t)k_eff)));
+  return 64 * cb + 63 - L2;
 }
 
 // Appends every key whose top bits reach the threshold bin to the request's
@@ -681,19 +688,39 @@ __global__ __launch_bounds__(256) void decode_collect_kernel(IndexerParams p) {
   __shared__ int sh_base;
   const int b = blockIdx.y;
   const int n_valid = decode_len(p.kv, b, p.pos_offset, p.n_k);
-  const int k_eff = min(p.topk, n_valid);
   if ((int)blockIdx.x * kDecodeCollectKeys >= n_valid) return;  // uniform: no keys here (or none at all)
-  const uint32_t tbin = (uint32_t)block_threshold_bin(p.dec_hist + (size_t)b * kDecodeHistBins, k_eff, scratch);
+  __shared__ int sh_tbin;
+  if (threadIdx.x < kWave) {
+    const int k_eff = min(p.topk, n_valid);
+    const int tb = wave_threshold_bin(p.dec_hist + (size_t)b * kDecodeHistStride, k_eff);
+    if (threadIdx.x == 0) sh_tbin = tb;
+  }
+  __syncthreads();
+  const uint32_t tbin = (uint32_t)sh_tbin;
   const int beg = blockIdx.x * kDecodeCollectKeys, end = min(beg + kDecodeCollectKeys, n_valid);
-  const uint32_t* keys = p.dec_keys + (size_t)b * p.n_k;
+  const uint32_t* keys = p.dec_keys + (size_t)b * decode_key_stride(p.n_k);
   constexpr int U = kDecodeCollectKeys / 256;
-  // thread t takes the U consecutive keys beg + U*t ..
+  static_assert(U == 16, "four 16-byte loads per thread");
+  // thread t takes the U consecutive keys beg + U*t .. with four 16-byte
+  // loads (rows are 256-byte aligned and padded to 64 keys, so a load that
+  // starts before `end` stays inside the row)
   uint32_t u[U];
+  {
+    const int i0 = beg + U * (int)threadIdx.x;
+    const uint4* src = (const uint4*)(keys + i0);
+#pragma unroll
+    for (int q = 0; q < U / 4; ++q) {
+      const uint4 v = i0 < end ? src[q] : make_uint4(0u, 0u, 0u, 0u);
+      u[4 * q] = v.x;
+      u[4 * q + 1] = v.y;
+      u[4 * q + 2] = v.z;
+      u[4 * q + 3] = v.w;
+    }
+  }
   int n = 0;
 #pragma unroll
   for (int j = 0; j < U; ++j) {
     const int i = beg + U * (int)threadIdx.x + j;
-    u[j] = i < end ? keys[i] : 0u;
     n += (i < end && (u[j] >> (32 - kDecodeHistBits)) >= tbin) ? 1 : 0;
   }
   int total;
@@ -738,9 +765,9 @@ static void launch_decode_scores_t(const IndexerParams& p, hipStream_t s) {
 }
 
 hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
-  // zero the histograms and the candidate counters that follow them (a
-  // kernel, not a memset node), and plan ragged score blocks
-  const size_t nz = (size_t)p.B * kDecodeHistBins + (size_t)p.B;
+  // zero the histograms and the counters that follow them (a kernel, not a
+  // memset node), and plan ragged score blocks
+  const size_t nz = (size_t)p.B * kDecodeHistStride + (size_t)p.B;
   hipLaunchKernelGGL(decode_prepare_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 1024)), dim3(256), 0,
                      s, p, nz, p.B + kDecodeTargetBlocks);
   hipError_t e = record_phase(p.ev, 0, s);

@@ -101,6 +101,19 @@ def test_decode_exact_integer(dsa):
     check_indexer(dsa, inp, 100, exact=True)
 
 
+@pytest.mark.parametrize("n_k,topk,qk,H,D", [
+    (9000, 2048, 3, 64, 128),   # hundreds of short runs of equal scores among the winners
+    (6000, 512, 1, 16, 32),     # a run longer than 32: re-sort with index passes (16-bit indices)
+    (70000, 2048, 1, 4, 32),    # the same with indices above 65535
+])
+def test_decode_tie_runs(dsa, n_k, topk, qk, H, D):
+    """Exact-integer scores with many equal values among the top-k but no list
+    overflow: equal scores must come out in index order."""
+    say(f"decode tie runs n_k={n_k} k={topk}")
+    inp = make_int_indexer_inputs(1, 1, n_k, H, D, seed=13, qk_range=qk)
+    check_indexer(dsa, inp, topk, exact=True)
+
+
 def test_decode_all_ties_overflow_path(dsa):
     """All scores equal: the candidate list overflows and the exact full-row
     select must return the k lowest indices in order."""
