@@ -22,6 +22,7 @@ from .gen import (  # noqa: F401
     PagedLayout,
     make_paged_layout,
     scatter_to_pages,
+    make_correlated_topk,
     to_e4m3_clipped,
     host_bits,
 )

@@ -216,6 +216,35 @@ def scatter_to_pages(flat: torch.Tensor, layout: PagedLayout, junk: torch.Tensor
     return pool
 
 
+def make_correlated_topk(n_layers: int, rows: int, k: int, n_k: int, *, swap: float, seed: int,
+                         reset_every: int = 0, short_rows: int = 0) -> np.ndarray:
+    """Synthetic per-layer top-k index rows [n_layers, rows, k] int32 whose
+    layers overlap like a random walk: layer 0's row is a random k-subset of
+    [0, n_k), and layer l's row is layer l-1's with round(swap * k) entries
+    replaced by fresh random tokens (a fresh subset every reset_every layers,
+    if > 0). The first short_rows rows hold only their row number + 1 <= k
+    valid entries (a causal prefix), padded with -1. Rows list their tokens in
+    random order."""
+    rng = np.random.default_rng(seed)
+    out = np.full((n_layers, rows, k), -1, dtype=np.int32)
+    m = int(round(swap * k))
+    for r in range(rows):
+        cnt = min(k, r + 1) if r < short_rows else k
+        pool = min(n_k, r + 1) if r < short_rows else n_k
+        cur = None
+        for l in range(n_layers):
+            if cur is None or (reset_every and l % reset_every == 0):
+                cur = rng.choice(pool, cnt, replace=False)
+            elif m and cnt < pool:
+                cur = cur.copy()
+                drop = rng.choice(cnt, min(m, cnt), replace=False)
+                fresh = np.setdiff1d(rng.choice(pool, min(pool, cnt + 2 * m), replace=False), cur)
+                take = min(len(drop), len(fresh))
+                cur[drop[:take]] = fresh[:take]
+            out[l, r, :cnt] = rng.permutation(cur)
+    return out
+
+
 def host_bits(t: Optional[torch.Tensor]):
     """Raw bits of a tensor as a numpy array on the host: bf16 -> uint16,
     float8_e4m3fn -> uint8, fp32 -> float32, int32 -> int32."""
