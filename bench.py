@@ -14,7 +14,8 @@ the stream it launches on. `cpu_baseline` times the fp64 CPU oracle on a
 bounded sample of the same layer's query rows and extrapolates by the number of
 causal keys. `extra` adds the bf16 200K layer, the 47-layer F/S prefill stack at
 L = 61440 (all-F, index_topk_freq 2 and 4), decode at 200K context and paged
-decode of 32 requests with ragged context lengths up to 200K.
+decode of 32 requests with ragged context lengths up to 200K, and the
+cross-layer top-k overlap of 47 layers.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -282,6 +283,36 @@ def paged_decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, page_siz
     return res
 
 
+def overlap_bench(dsa, torch, steps, n=47, R=256, k=2048, n_k=200000):
+    """Cross-layer top-k overlap of 47 layers' indices for 256 sampled query
+    rows (k = 2048 of a 200K context; synthetic correlated random-walk index
+    sets), then the 12-F similarity pattern from it. Bytes: every workgroup
+    (row, layer a) reads the rows of layers b >= a, (n + 1) n / 2 rows of k
+    int32 per query row, from L2; n R k int32 are the compulsory HBM reads."""
+    from dsa_inputs import make_correlated_topk
+    idx = torch.from_numpy(make_correlated_topk(n, R, k, n_k, swap=0.1, seed=47, reset_every=6)).cuda()
+    out = dsa.topk_overlap(idx, n_k)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        dsa.topk_overlap(idx, n_k, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    t0 = time.perf_counter()
+    pat = dsa.similarity_pattern(out, 12)
+    pat_ms = (time.perf_counter() - t0) * 1e3
+    l2_bytes = R * (n + 1) * n // 2 * k * 4
+    res = {"layers": n, "rows": R, "topk": k, "n_k": n_k, "ms": ms, "l2_read_GBps": l2_bytes / ms / 1e6,
+           "compulsory_hbm_GBps": n * R * k * 4 / ms / 1e6, "pattern_12F": pat, "pattern_host_ms": pat_ms}
+    log(f"topk overlap {n} layers x {R} rows: {ms:.3f} ms ({res['l2_read_GBps']:.0f} GB/s of index rows), "
+        f"pattern {pat_ms:.2f} ms on the host")
+    del idx, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def quant_bench(dsa, torch, L, steps):
     """Per-token fp8 quantisation of the 200K layer's q_idx ([L, 64 * 128] bf16):
     algorithmic HBM bytes = 2 read + 1 written per element + 4 per row."""
@@ -328,7 +359,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline + CPU baseline only")
     ap.add_argument("--stack-L", type=int, default=61440)
     ap.add_argument("--stack-layers", type=int, default=47)
-    ap.add_argument("--only", choices=["stack", "stack200k", "decode", "paged", "quant"], default=None,
+    ap.add_argument("--only", choices=["stack", "stack200k", "decode", "paged", "quant", "overlap"], default=None,
                     help="run only the stack or only the decode measurement and print its JSON "
                          "(for profiling one part; not the benchmark line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -372,6 +403,9 @@ def main():
     if args.only == "decode":
         print(json.dumps({f"decode_B{B}": decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
                           for B in (1, 32)}), flush=True)
+        return
+    if args.only == "overlap":
+        print(json.dumps(overlap_bench(dsa, torch, max(2, args.steps))), flush=True)
         return
     if args.only == "paged":
         print(json.dumps(paged_decode_bench(dsa, torch, 32, 200000, 47, topk, args.steps, 2)), flush=True)
@@ -449,6 +483,7 @@ def main():
             extra[f"decode_B{B}"] = decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
         log("paged ragged decode B=32")
         extra["decode_paged_ragged_B32"] = paged_decode_bench(dsa, torch, 32, 200000, 47, topk, args.steps, 2)
+        extra["topk_overlap_47_layers"] = overlap_bench(dsa, torch, max(2, args.steps))
         result["extra"] = extra
     print(json.dumps(result), flush=True)
 

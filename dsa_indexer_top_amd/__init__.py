@@ -19,6 +19,8 @@ from .api import (  # noqa: F401
     paged_indexer_topk,
     paged_sparse_attn,
     quantize_fp8_rows,
+    similarity_pattern,
+    topk_overlap,
     resolve_pattern,
     sparse_attn,
 )

@@ -32,6 +32,8 @@ EXPORTS = (
     "dsa_paged_sparse_attn",
     "dsa_paged_layer_stack_run",
     "dsa_paged_append_rows",
+    "dsa_topk_overlap",
+    "dsa_similarity_pattern",
     "dsa_status_string",
     "dsa_last_error",
 )
@@ -124,6 +126,10 @@ def load() -> ctypes.CDLL:
     lib.dsa_paged_layer_stack_run.argtypes = [POINTER(StackArgs), POINTER(PagedKVArgs), c_char_p, c_int32, c_void_p]
     lib.dsa_paged_append_rows.restype = c_int32
     lib.dsa_paged_append_rows.argtypes = [c_void_p, c_int32, c_int32, c_void_p, POINTER(PagedKVArgs), c_void_p]
+    lib.dsa_topk_overlap.restype = c_int32
+    lib.dsa_topk_overlap.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]
+    lib.dsa_similarity_pattern.restype = c_int32
+    lib.dsa_similarity_pattern.argtypes = [c_int32, POINTER(ctypes.c_int64), c_int32, ctypes.c_char_p]
     lib.dsa_quantize_fp8_rows.restype = c_int32
     lib.dsa_quantize_fp8_rows.argtypes = [c_void_p, ctypes.c_int64, c_int32, c_void_p, c_void_p, c_void_p]
     lib.dsa_status_string.restype = c_char_p

@@ -363,6 +363,39 @@ def paged_append_rows(src: torch.Tensor, pool: torch.Tensor, kv: PagedKV, stream
                                           _stream(stream)))
 
 
+def topk_overlap(idx: torch.Tensor, n_k: int, *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dsa_topk_overlap: idx [n_layers, rows, topk] int32 (GPU) -> inter
+    [n_layers, n_layers] int64 (GPU), inter[a][b] = sum over rows of the number
+    of tokens both layers selected. The overlap ratio is inter[a][b] / inter[a][a]."""
+    _need(idx, "idx", dtype=torch.int32, ndim=3)
+    n_layers, rows, topk = idx.shape
+    if out is None:
+        out = torch.empty((n_layers, n_layers), dtype=torch.int64, device=idx.device)
+    else:
+        _need(out, "out", dtype=torch.int64)
+        if tuple(out.shape) != (n_layers, n_layers):
+            raise ValueError("out must be [n_layers, n_layers]")
+    _check(L.load().dsa_topk_overlap(_ptr(idx), n_layers, rows, topk, int(n_k), _ptr(out), _stream(stream)))
+    return out
+
+
+def similarity_pattern(inter, n_full: int) -> str:
+    """dsa_similarity_pattern (host): the F/S string with n_full F layers that
+    maximises the selections every S layer shares with the last F layer before
+    it. inter: [n_layers, n_layers] int64 (torch tensor on any device, or array)."""
+    if isinstance(inter, torch.Tensor):
+        inter = inter.detach().to("cpu", torch.int64).contiguous()
+    else:
+        inter = torch.as_tensor(inter, dtype=torch.int64).contiguous()
+    n = inter.shape[0]
+    if inter.dim() != 2 or inter.shape[1] != n:
+        raise ValueError("inter must be square")
+    buf = ctypes.create_string_buffer(n + 1)
+    ptr = ctypes.cast(inter.data_ptr(), ctypes.POINTER(ctypes.c_int64))
+    _check(L.load().dsa_similarity_pattern(n, ptr, int(n_full), buf))
+    return buf.value.decode()
+
+
 def quantize_fp8_rows(x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
                       scale: Optional[torch.Tensor] = None, stream=None):
     """Per-token fp8 quantisation (dsa_quantize_fp8_rows): x is bf16 with the

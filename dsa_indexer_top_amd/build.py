@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["dsa_api.cpp", "indexer_prefill.hip", "topk_select.hip", "sparse_attn.hip", "quant.hip", "paged.hip"]
+SOURCES = ["dsa_api.cpp", "indexer_prefill.hip", "topk_select.hip", "sparse_attn.hip", "quant.hip", "paged.hip", "overlap.hip"]
 
 # -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32 (only the device pass
 # knows the feature; the host pass warns and ignores it).

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 #include <string>
 
 #include "dsa.h"
@@ -43,6 +44,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int kMaxTopk = 2048;
 constexpr int kMaxAttnTopk = 4096;
 constexpr int kMaxB = 65535;
+constexpr int kMaxOverlapLayers = 1024;
+constexpr int kMaxOverlapKeys = 1 << 19;  // 64 KB of LDS bitmap
 
 dsa_status check_indexer_shape(const dsa_indexer_args* a, const char* what) {
   if (!a) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: args is NULL", what);
@@ -542,6 +545,68 @@ dsa_status dsa_paged_append_rows(const void* src, int32_t B, int32_t row_bytes, 
     return fail(DSA_ERR_INVALID_ARGUMENT, "%s: src and pool are required (4-byte aligned)", what);
   const hipError_t e = dsa::launch_paged_append_rows(src, B, row_bytes, pool, pk, kv->max_seq_len, (hipStream_t)stream);
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+dsa_status dsa_topk_overlap(const int32_t* idx, int32_t n_layers, int32_t rows, int32_t topk, int32_t n_k,
+                            int64_t* inter, void* stream) {
+  const char* what = "topk_overlap";
+  if (n_layers < 1 || n_layers > kMaxOverlapLayers)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: n_layers=%d out of 1..%d", what, n_layers, kMaxOverlapLayers);
+  if (rows < 1 || topk < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: rows=%d topk=%d must be >= 1", what, rows, topk);
+  if (n_k < 1 || n_k > kMaxOverlapKeys)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: n_k=%d out of 1..%d (the bitmap lives in LDS)", what, n_k, kMaxOverlapKeys);
+  int64_t n;
+  if (!count4(n_layers, rows, topk, 4, &n)) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: sizes overflow int64", what);
+  if (!idx || !inter || !aligned(idx, 4) || !aligned(inter, 8))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: idx (4-byte aligned) and inter (8-byte aligned) are required", what);
+  const hipError_t e = dsa::launch_topk_overlap(idx, n_layers, rows, topk, n_k, inter, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+dsa_status dsa_similarity_pattern(int32_t n_layers, const int64_t* inter, int32_t n_full, char* out) {
+  const char* what = "similarity_pattern";
+  if (!inter || !out) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: inter and out are required", what);
+  if (n_layers < 1 || n_layers > kMaxOverlapLayers)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: n_layers=%d out of 1..%d", what, n_layers, kMaxOverlapLayers);
+  if (n_full < 1 || n_full > n_layers)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: n_full=%d out of 1..%d", what, n_full, n_layers);
+  const int L = n_layers;
+  for (int64_t i = 0; i < (int64_t)L * L; ++i)
+    if (inter[i] < 0 || inter[i] > ((int64_t)1 << 52))
+      return fail(DSA_ERR_INVALID_ARGUMENT, "%s: inter[%lld] = %lld outside 0..2^52", what, (long long)i,
+                  (long long)inter[i]);
+  // seg(i, e) = sum_{i < l < e} inter[i][l]: prefix sums of each row
+  std::vector<int64_t> pre((size_t)L * (L + 1), 0);
+  for (int i = 0; i < L; ++i)
+    for (int l = 0; l < L; ++l) pre[(size_t)i * (L + 1) + l + 1] = pre[(size_t)i * (L + 1) + l] + inter[(size_t)i * L + l];
+  auto seg = [&](int i, int e) { return pre[(size_t)i * (L + 1) + e] - pre[(size_t)i * (L + 1) + i + 1]; };
+  // V[i][j]: best shared selections of layers i..L-1 with layer i F and j F
+  // layers in i..L-1 (-1: impossible)
+  const int J = n_full;
+  std::vector<int64_t> V((size_t)(L + 1) * (J + 1), -1);
+  auto at = [&](int i, int j) -> int64_t& { return V[(size_t)i * (J + 1) + j]; };
+  for (int i = L - 1; i >= 0; --i) {
+    at(i, 1) = seg(i, L);
+    for (int j = 2; j <= J && j <= L - i; ++j) {
+      int64_t best = -1;
+      for (int e = i + 1; e <= L - j + 1; ++e)
+        if (at(e, j - 1) >= 0) best = std::max(best, seg(i, e) + at(e, j - 1));
+      at(i, j) = best;
+    }
+  }
+  // F layers front to back: the smallest next F layer that keeps the optimum
+  for (int l = 0; l < L; ++l) out[l] = 'S';
+  out[L] = '\0';
+  out[0] = 'F';
+  for (int i = 0, j = J; j > 1; --j) {
+    const int64_t target = at(i, j);
+    int e = i + 1;
+    while (!(at(e, j - 1) >= 0 && seg(i, e) + at(e, j - 1) == target)) ++e;
+    out[e] = 'F';
+    i = e;
+  }
   return ok();
 }
 

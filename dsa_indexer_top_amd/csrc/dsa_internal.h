@@ -121,6 +121,8 @@ hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_paged_append_rows(const void* src, int B, int row_bytes, void* pool, const PagedKV& kv,
                                     int max_seq_len, hipStream_t s);
+hipError_t launch_topk_overlap(const int32_t* idx, int n_layers, int rows, int topk, int n_k, int64_t* inter,
+                               hipStream_t s);
 hipError_t launch_quantize_fp8_rows(const void* x, int64_t rows, int cols, void* out, float* scale, hipStream_t s);
 
 }  // namespace dsa

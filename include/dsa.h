@@ -285,6 +285,36 @@ dsa_status dsa_paged_append_rows(const void *src, int32_t B, int32_t row_bytes, 
 dsa_status dsa_quantize_fp8_rows(const void *x, int64_t rows, int32_t cols, void *out, float *scale,
                                  void *stream);
 
+/* Cross-layer top-k overlap, the measurement behind IndexCache (paper
+ * appendix, Figure 4: pairwise overlap of the layers' top-k index sets; the
+ * repository page's "Key Insight": adjacent layers share most of theirs).
+ *   idx    device int32 [n_layers, rows, topk]: row r of layer l lists the
+ *          selected tokens of the same query r in every layer (e.g. the
+ *          indexer's out_idx per layer). Entries < 0 or >= n_k are ignored;
+ *          the valid entries of a row must be distinct (as the indexer's are).
+ *   inter  device int64 [n_layers, n_layers], overwritten:
+ *          inter[a][b] = sum_r |S_a(r) & S_b(r)|, S_l(r) the valid entries of
+ *          row r of layer l; inter[a][a] = sum_r |S_a(r)|. The overlap ratio
+ *          of a and b is inter[a][b] / inter[a][a].
+ * 1 <= n_layers <= 1024, rows >= 1, topk >= 1, 1 <= n_k <= 2^19 (one bit per
+ * token in LDS), else INVALID_ARGUMENT / UNSUPPORTED. Asynchronous on stream. */
+dsa_status dsa_topk_overlap(const int32_t *idx, int32_t n_layers, int32_t rows, int32_t topk, int32_t n_k,
+                            int64_t *inter, void *stream);
+
+/* Similarity-based layer pattern from an overlap matrix (the training-free
+ * "similarity-based searched pattern" of the paper's Table 5; the pages do
+ * not give the search, the plain reading is taken): among the patterns with
+ * n_full F layers, layer 0 always F, the one that maximises
+ *   sum over S layers l of inter[f(l)][l],  f(l) = the last F layer before l
+ * (the layer whose cached indices l reuses, paper Figure 2 caption), i.e. the
+ * number of selections each S layer shares with its source. The optimum is
+ * exact (a segment recursion, O(n_full * n_layers^2)); among equal totals the
+ * lexicographically smallest list of F layers wins. inter: HOST int64
+ * [n_layers, n_layers] with entries in 0..2^52 (dsa_topk_overlap's output);
+ * out: HOST buffer of n_layers + 1 bytes ('F'/'S' string, NUL-terminated),
+ * usable as dsa_layer_stack_run's pattern. Pure host code; needs no GPU. */
+dsa_status dsa_similarity_pattern(int32_t n_layers, const int64_t *inter, int32_t n_full, char *out);
+
 /* Static text of a status code. */
 const char *dsa_status_string(dsa_status status);
 
