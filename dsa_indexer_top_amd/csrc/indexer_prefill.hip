@@ -325,9 +325,34 @@ void indexer_prefill_kernel(IndexerParams p) {
   // before the barrier of iteration t + 1 completes it, a whole tile of MFMA
   // work later. No registers hold the tile on the way.
   const unsigned char* kbase = (const unsigned char*)p.k + (size_t)b * p.n_k * T::kRowBytes;
+  // fp8: the lane offsets of this wave's 16-byte slots inside a full tile are
+  // fixed for the whole row and kept in registers (a lane whose slot is a
+  // row's padding loads that row's first chunk into the padding, which is
+  // never read), so a full tile's load costs one address add per instruction;
+  // the fp8 epilogue is bound by VALU work. bf16 has no registers to spare and
+  // recomputes them.
+  static_assert(T::kSlots % kWave == 0, "a load instruction is all slots or none");
+  uint32_t voff[FP8 ? CPT : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int q = c * NT + wave * kWave + lane;
+      const int r = q / T::kSlotsPerRow;
+      const int col = q - r * T::kSlotsPerRow;
+      voff[c] = (uint32_t)(r * T::kRowBytes + 16 * (col < T::kChunksPerRow ? col : 0));
+    }
+  }
   auto dma_tile = [&](int tile, int buf) {
     const unsigned char* src = kbase + (size_t)tile * kTileKeys * T::kRowBytes;
     const int rows_left = p.n_k - tile * kTileKeys;
+    if (FP8 && rows_left >= kTileKeys) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int q0 = c * NT + wave * kWave;  // first 16-byte LDS slot of this wave's load (uniform)
+        if (q0 < T::kSlots) lds_load16(src + voff[FP8 ? c : 0], &lds_k[buf][16 * q0]);
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int q0 = c * NT + wave * kWave;  // first 16-byte LDS slot of this wave's load (uniform)
