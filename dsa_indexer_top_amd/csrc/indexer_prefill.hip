@@ -325,31 +325,37 @@ void indexer_prefill_kernel(IndexerParams p) {
   // before the barrier of iteration t + 1 completes it, a whole tile of MFMA
   // work later. No registers hold the tile on the way.
   const unsigned char* kbase = (const unsigned char*)p.k + (size_t)b * p.n_k * T::kRowBytes;
-  // fp8: the lane offsets of this wave's 16-byte slots inside a full tile are
-  // fixed for the whole row and kept in registers (a lane whose slot is a
-  // row's padding loads that row's first chunk into the padding, which is
-  // never read), so a full tile's load costs one address add per instruction;
-  // the fp8 epilogue is bound by VALU work. bf16 has no registers to spare and
-  // recomputes them.
+  // The lane offsets of this wave's 16-byte slots inside a full tile are
+  // fixed for the whole row and kept in registers, two 16-bit offsets per
+  // register (a lane whose slot is a row's padding loads that row's first
+  // chunk into the padding, which is never read), so a full tile's load is a
+  // scalar base plus a 32-bit lane offset: no 64-bit address math and no
+  // exec-mask branch per instruction. The epilogue leaves little VALU time.
   static_assert(T::kSlots % kWave == 0, "a load instruction is all slots or none");
-  uint32_t voff[FP8 ? CPT : 1];
-  if constexpr (FP8) {
+  uint32_t voff[(CPT + 1) / 2];  // two 16-bit offsets per register (a tile is < 64 KB)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int q = c * NT + wave * kWave + lane;
-      const int r = q / T::kSlotsPerRow;
-      const int col = q - r * T::kSlotsPerRow;
-      voff[c] = (uint32_t)(r * T::kRowBytes + 16 * (col < T::kChunksPerRow ? col : 0));
-    }
+  for (int c = 0; c < (CPT + 1) / 2; ++c) voff[c] = 0u;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int q = c * NT + wave * kWave + lane;
+    const int r = q / T::kSlotsPerRow;
+    const int col = q - r * T::kSlotsPerRow;
+    voff[c / 2] |= (uint32_t)(r * T::kRowBytes + 16 * (col < T::kChunksPerRow ? col : 0)) << (16 * (c & 1));
   }
   auto dma_tile = [&](int tile, int buf) {
     const unsigned char* src = kbase + (size_t)tile * kTileKeys * T::kRowBytes;
     const int rows_left = p.n_k - tile * kTileKeys;
-    if (FP8 && rows_left >= kTileKeys) {
+    if (rows_left >= kTileKeys) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int q0 = c * NT + wave * kWave;  // first 16-byte LDS slot of this wave's load (uniform)
-        if (q0 < T::kSlots) lds_load16(src + voff[FP8 ? c : 0], &lds_k[buf][16 * q0]);
+        if (q0 < T::kSlots) {
+          // extracted here, not hoisted: the load then takes it as a 32-bit
+          // offset to the scalar base
+          uint32_t o = (voff[c / 2] >> (16 * (c & 1))) & 0xFFFFu;
+          asm volatile("" : "+v"(o));
+          lds_load16(src + o, &lds_k[buf][16 * q0]);
+        }
       }
       return;
     }
