@@ -479,9 +479,10 @@ void indexer_prefill_kernel(IndexerParams p) {
     const uint64_t am = ballot(valid && f_score > theta_f);
     if (am) {
       if ((am >> lane) & 1ull) {
-        const int pos = cnt + mbcnt(am);
-        ckey[pos] = score_key(f_score);
-        cidx[pos] = key;
+        // 32-bit byte offset from the row's (scalar) list bases: no 64-bit address math
+        const uint32_t off = 4u * (uint32_t)(cnt + mbcnt(am));
+        *(uint32_t*)((unsigned char*)ckey + off) = score_key(f_score);
+        *(int32_t*)((unsigned char*)cidx + off) = key;
       }
       cnt += popc64(am);
       if (cnt > p.C - 3 * kTileKeys && lane == 0) atomicOr(&shl.flags[par], 1u << wave);
