@@ -8,16 +8,17 @@
 
 namespace dsa {
 
-// Candidate-list capacity per query row, 4k (at least k + 256), in both
+// Candidate-list capacity per query row, 4k (at least k + 512), in both
 // paths. Prefill (streaming filter): room for the kept superset of the top-k
-// plus new arrivals; a shrink costs about C / (C - k) list passes per
-// accepted key. Decode (one threshold pass): every key whose 12-bit histogram
-// bin reaches the k-th key's bin, i.e. k plus most of one bin; a larger list
-// sends the request to the exact full-row select.
+// plus the 256 appends a nearly full list may still receive before its shrink;
+// a shrink costs about C / (C - k) list passes per accepted key. Decode (one
+// threshold pass): every key whose 12-bit histogram bin reaches the k-th
+// key's bin, i.e. k plus most of one bin; a larger list sends the request to
+// the exact full-row select.
 inline int cand_capacity(int topk, bool decode) {
   (void)decode;
   int c = topk * 4;
-  if (c < topk + 256) c = topk + 256;
+  if (c < topk + 512) c = topk + 512;
   return (c + 63) / 64 * 64;
 }
 

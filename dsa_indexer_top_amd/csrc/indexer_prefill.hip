@@ -10,8 +10,8 @@
 // Mapping (gfx950, wave64). A workgroup owns 4 consecutive query rows, one per
 // wave. A wave holds its row's indexer queries as MFMA A-fragments in
 // registers (heads are the M dimension, padded to 32 or 64 rows) and streams
-// 64-key tiles of k through double-buffered, padded LDS (keys are the N
-// dimension, head_dim the K dimension). v_mfma_f32_32x32x16_bf16 (fp8:
+// k through double-buffered, padded LDS, 128 keys per loop iteration (keys are
+// the N dimension, head_dim the K dimension). v_mfma_f32_32x32x16_bf16 (fp8:
 // v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales) produces a 32 heads x 32
 // keys block per lane group; in that layout a lane holds 16 heads of one key,
 // so ReLU, the head weights and the head sum are per-lane FMAs, and one
@@ -42,7 +42,11 @@ namespace dsa {
 template <bool FP8>
 constexpr int prefill_waves() { return 4; }
 constexpr int kMaxPrefillWaves = 8;
-constexpr int kTileKeys = 64;
+constexpr int kTileKeys = 64;                  // keys per LDS sub-tile and per filter commit
+constexpr int kIterKeys = 2 * kTileKeys;       // keys per loop iteration (one barrier)
+// Appends a list may receive between the commit that flags it as nearly full
+// and the shrink that serves the flag: the flagging commit and three more.
+constexpr int kListMargin = 4 * kTileKeys;
 
 template <int D, bool FP8>
 struct KTile {
@@ -73,7 +77,7 @@ struct ShrinkLds {
   uint32_t hist[256 * kShrinkHistCopies];
   int scan[kMaxPrefillWaves + 1];
   int res[4];                       // digit, keys above the digit, keys in the digit
-  uint32_t flags[2];                // bit w: the row of wave w needs a shrink (by parity)
+  uint32_t flags[3];                // bit w: the row of wave w needs a shrink (iteration mod 3)
   int cnt[kMaxPrefillWaves];        // that row's list length (in), new length (out)
   uint32_t theta[kMaxPrefillWaves]; // new acceptance threshold (out)
 };
@@ -263,7 +267,7 @@ void indexer_prefill_kernel(IndexerParams p) {
   constexpr int NT = kPrefillWaves * kWave;
   constexpr int KS = FP8 ? D / 64 : D / 16;  // MFMA k-steps over head_dim
   constexpr int CPT = (T::kSlots + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][T::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][2 * T::kBytes];
   __shared__ ShrinkLds shl;
 
   const int lane = lane_id();
@@ -277,7 +281,7 @@ void indexer_prefill_kernel(IndexerParams p) {
   const int t_last = min(qb * kPrefillWaves + kPrefillWaves, p.n_q) - 1;
   const int kend_wg = min(p.pos_offset + t_last + 1, p.n_k);
   const int kend = active ? min(p.pos_offset + t + 1, p.n_k) : 0;
-  const int n_tiles = (kend_wg + kTileKeys - 1) / kTileKeys;
+  const int n_tiles = (kend_wg + kIterKeys - 1) / kIterKeys;
   const int i32 = lane & 31;
   const int g = lane >> 5;
 
@@ -342,9 +346,10 @@ void indexer_prefill_kernel(IndexerParams p) {
     const int col = q - r * T::kSlotsPerRow;
     voff[c / 2] |= (uint32_t)(r * T::kRowBytes + 16 * (col < T::kChunksPerRow ? col : 0)) << (16 * (c & 1));
   }
-  auto dma_tile = [&](int tile, int buf) {
-    const unsigned char* src = kbase + (size_t)tile * kTileKeys * T::kRowBytes;
-    const int rows_left = p.n_k - tile * kTileKeys;
+  auto dma_sub = [&](int sub, unsigned char* dst) {
+    const unsigned char* src = kbase + (size_t)sub * kTileKeys * T::kRowBytes;
+    const int rows_left = p.n_k - sub * kTileKeys;
+    if (rows_left <= 0) return;  // wholly past n_k: never a valid key
     if (rows_left >= kTileKeys) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
@@ -354,7 +359,7 @@ void indexer_prefill_kernel(IndexerParams p) {
           // offset to the scalar base
           uint32_t o = (voff[c / 2] >> (16 * (c & 1))) & 0xFFFFu;
           asm volatile("" : "+v"(o));
-          lds_load16(src + o, &lds_k[buf][16 * q0]);
+          lds_load16(src + o, dst + 16 * q0);
         }
       }
       return;
@@ -368,9 +373,15 @@ void indexer_prefill_kernel(IndexerParams p) {
         const int col = q - r * T::kSlotsPerRow;
         const int rr = r < rows_left ? r : rows_left - 1;  // rows past n_k repeat the last (masked later)
         if (col < T::kChunksPerRow && r < kTileKeys)
-          lds_load16(src + (size_t)rr * T::kRowBytes + 16 * col, &lds_k[buf][16 * q0]);
+          lds_load16(src + (size_t)rr * T::kRowBytes + 16 * col, dst + 16 * q0);
       }
     }
+  };
+
+  // an iteration's tile is two sub-tiles, back to back in one buffer
+  auto dma_tile = [&](int tile, int buf) {
+    dma_sub(2 * tile, lds_k[buf]);
+    dma_sub(2 * tile + 1, lds_k[buf] + T::kBytes);
   };
 
   uint32_t theta = 0u;
@@ -468,8 +479,8 @@ void indexer_prefill_kernel(IndexerParams p) {
     f_score = score;
     asm volatile("" : "+v"(f_score));
   };
-  // par: parity of the iteration; a full list raises flag bit `wave` of
-  // flags[par], which the workgroup serves after the next barrier.
+  // par: the iteration mod 3; a full list raises flag bit `wave` of
+  // flags[par], which the workgroup reads after the next barrier and serves.
   auto filter_commit = [&](int par) {
     const int key = pend_base + lane;
     const bool valid = key < pend_end;
@@ -485,7 +496,7 @@ void indexer_prefill_kernel(IndexerParams p) {
         *(int32_t*)((unsigned char*)cidx + off) = key;
       }
       cnt += popc64(am);
-      if (cnt > p.C - 3 * kTileKeys && lane == 0) atomicOr(&shl.flags[par], 1u << wave);
+      if (cnt > p.C - kListMargin && lane == 0) atomicOr(&shl.flags[par], 1u << wave);
     }
     pend_end = 0;
   };
@@ -498,13 +509,13 @@ void indexer_prefill_kernel(IndexerParams p) {
     __syncthreads();
 #pragma unroll 1
     for (int w = 0; w < kPrefillWaves; ++w) {
-      if (!((flags >> w) & 1u) || shl.cnt[w] <= p.C - 3 * kTileKeys) continue;
+      if (!((flags >> w) & 1u) || shl.cnt[w] <= p.C - kListMargin) continue;
       const size_t rw = (size_t)b * p.n_q + qb * kPrefillWaves + w;
-      coop_shrink<kPrefillWaves>(p.cand_key + rw * p.C, p.cand_idx + rw * p.C, shl.cnt[w], p.topk, p.C - 3 * kTileKeys, shl,
+      coop_shrink<kPrefillWaves>(p.cand_key + rw * p.C, p.cand_idx + rw * p.C, shl.cnt[w], p.topk, p.C - kListMargin, shl,
                   &shl.theta[w], &shl.cnt[w]);
       __syncthreads();
     }
-    if (((flags >> wave) & 1u) && cnt > p.C - 3 * kTileKeys) {
+    if (((flags >> wave) & 1u) && cnt > p.C - kListMargin) {
       theta = uniform_u(shl.theta[wave]);
       theta_f = key_score(theta);
       cnt = uniform_i(shl.cnt[wave]);
@@ -521,63 +532,85 @@ void indexer_prefill_kernel(IndexerParams p) {
   if (threadIdx.x == 0) {
     shl.flags[0] = 0u;
     shl.flags[1] = 0u;
+    shl.flags[2] = 0u;
   }
   // Nothing may stay in flight into the loop: the loop's own prefetches are
   // then the only outstanding loads the MFMAs could be made to wait for.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (kend > 0) half_step(FalseT{}, TrueT{}, lds_k[0], 0, accA, accB, no_side);
-  // One tile: second half-tile of `tile` (+ epilogue of its first half, + the
-  // previous tile's filter), then the barrier that publishes tile+1, the load
-  // of tile+2 into the buffer `tile` leaves, then the first half of tile+1
-  // (+ epilogue of tile's second half); `tile` is then pending for the filter.
+  // One iteration, tile = 128 keys in four 32-key quarters q0..q3 (q0 was
+  // multiplied in the previous iteration): q1 (+ epilogue of q0, + the filter
+  // of the previous tile's keys 64..127, committed right after), q2 (+ epilogue
+  // of q1), q3 (+ epilogue of q2, + the filter of keys 0..63), the barrier that
+  // publishes tile+1, the commit of keys 0..63, the load of tile+2 into the
+  // buffer `tile` leaves, and q0 of tile+1 (+ epilogue of q3). Keys 64..127
+  // are then pending for the filter.
   auto iteration = [&](int tile) {
     const int cur = tile & 1;
     const bool more = tile + 1 < n_tiles;
-    const int base = tile * kTileKeys;
+    const int base = tile * kIterKeys;
     const bool mine = base < kend;                          // wave-uniform
-    const bool mine_next = more && base + kTileKeys < kend;
-    float ksc = 1.0f;
-    if constexpr (FP8) ksc = (mine && base + lane < kend) ? kscale[base + lane] : 0.0f;
-    float part0 = 0.0f, part1 = 0.0f;
-    const int par = tile & 1;
-    if (mine) part0 = half_step(TrueT{}, TrueT{}, lds_k[cur], 1, accB, accA, filter_compute);
+    const bool mine_next = more && base + kIterKeys < kend;
+    float ksc0 = 1.0f, ksc1 = 1.0f;
+    if constexpr (FP8) {
+      ksc0 = (mine && base + lane < kend) ? kscale[base + lane] : 0.0f;
+      ksc1 = (mine && base + kTileKeys + lane < kend) ? kscale[base + kTileKeys + lane] : 0.0f;
+    }
+    // Flag words rotate over three iterations: iteration t writes word t % 3
+    // (one commit before its barrier, one after), iteration t+1 reads it
+    // after its barrier and serves it. A wave may already be committing the
+    // keys of iteration t+2 (before barrier t+2) while a slower one still
+    // reads word t % 3, so t+2 must write another word: with two words the
+    // waves could read different values and enter different barriers.
+    const int par = tile % 3, prev = (tile + 2) % 3;
+    float q0 = 0.0f, q1 = 0.0f, q2 = 0.0f, q3 = 0.0f;
+    if (mine) q0 = half_step(TrueT{}, TrueT{}, lds_k[cur], 1, accB, accA, filter_compute);
     else filter_compute();
+    filter_commit(par);  // the previous tile's keys 64..127
+    if (mine) {
+      q1 = half_step(TrueT{}, TrueT{}, lds_k[cur], 2, accA, accB, no_side);
+      pend_p0 = q0;
+      pend_p1 = q1;
+      pend_ksc = ksc0;
+      pend_base = base;
+      pend_end = kend;
+      q2 = half_step(TrueT{}, TrueT{}, lds_k[cur], 3, accB, accA, filter_compute);
+    } else {
+      filter_compute();
+    }
     // this wave's load of tile+1 (issued one iteration ago) must have landed
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // Appends go out right after the barrier: the next wait on the vector
-    // memory counter (for the next K tile) is then half a tile away, so the
-    // stores' acknowledgements are not waited for on the spot.
-    filter_commit(par);
-    // The flags raised by the previous iteration's commits (other parity) are
-    // visible now; read them during the next half tile and serve them after
-    // it (the word is next written two iterations later, after a barrier).
+    filter_commit(par);  // keys 0..63
+    // The flags raised by the previous iteration's commits are visible now;
+    // read them during the next quarter and serve them after it (the word is
+    // next written two iterations later, after the next barrier).
     uint32_t flags_v = 0u;
-    auto read_flags = [&]() { flags_v = shl.flags[par ^ 1]; };
+    auto read_flags = [&]() { flags_v = shl.flags[prev]; };
     if (tile + 2 < n_tiles) dma_tile(tile + 2, cur);
     if (mine) {
       if (mine_next)
-        part1 = half_step(TrueT{}, TrueT{}, lds_k[cur ^ 1], 0, accA, accB, read_flags);
+        q3 = half_step(TrueT{}, TrueT{}, lds_k[cur ^ 1], 0, accA, accB, read_flags);
       else
-        part1 = half_step(TrueT{}, FalseT{}, lds_k[cur], 0, accA, accB, read_flags);
-      pend_p0 = part0;
-      pend_p1 = part1;
-      pend_ksc = ksc;
-      pend_base = base;
+        q3 = half_step(TrueT{}, FalseT{}, lds_k[cur], 0, accA, accB, read_flags);
+      pend_p0 = q2;
+      pend_p1 = q3;
+      pend_ksc = ksc1;
+      pend_base = base + kTileKeys;
       pend_end = kend;
     } else {
       read_flags();
     }
-    coop_shrinks(uniform_u(flags_v), par ^ 1);
+    coop_shrinks(uniform_u(flags_v), prev);
   };
   for (int tile = 0; tile < n_tiles; ++tile) iteration(tile);
   filter_compute();
   __syncthreads();
-  filter_commit(n_tiles & 1);
+  filter_commit(n_tiles % 3);
   __syncthreads();
-  coop_shrinks(uniform_u(shl.flags[(n_tiles & 1) ^ 1]), (n_tiles & 1) ^ 1);
-  coop_shrinks(uniform_u(shl.flags[n_tiles & 1]), n_tiles & 1);
+  coop_shrinks(uniform_u(shl.flags[(n_tiles + 2) % 3]), (n_tiles + 2) % 3);
+  coop_shrinks(uniform_u(shl.flags[n_tiles % 3]), n_tiles % 3);
   if (active && lane == 0) p.cand_cnt[row] = cnt;
 }
 
