@@ -35,7 +35,12 @@ __device__ __forceinline__ float canon_zero(float s) {
   return __uint_as_float(b == 0x80000000u ? 0u : b);
 }
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
+// (the range lets the compiler narrow lane arithmetic and fold lane guards)
+__device__ __forceinline__ int lane_id() {
+  const int l = __lane_id();
+  __builtin_assume(l >= 0 && l < kWave);
+  return l;
+}
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 

@@ -272,6 +272,9 @@ void indexer_prefill_kernel(IndexerParams p) {
 
   const int lane = lane_id();
   const int wave = uniform_i(threadIdx.x >> 6);  // wave-uniform: row state lives in SGPRs
+  // a range the compiler cannot see: folds the per-wave guards of the tile
+  // loads (1% fewer cycles; lane_id carries the lane's range)
+  __builtin_assume(wave >= 0 && wave < kPrefillWaves);
   const int nqb = (p.n_q + kPrefillWaves - 1) / kPrefillWaves;
   const int qb = nqb - 1 - (int)blockIdx.x;  // longest rows first
   const int b = blockIdx.y;

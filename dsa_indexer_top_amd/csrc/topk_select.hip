@@ -492,6 +492,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
   __shared__ uint32_t hist[kDecodeHistBins];
   __shared__ __attribute__((aligned(16))) unsigned char tile[4][T::BYTES];
   const int lane = lane_id(), wave = uniform_i(threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < 4);
   int b, k0, k1;
   if (p.kv.seq_lens) {
     // ragged lengths: this block's (request, key range) from the device-side plan
