@@ -23,7 +23,7 @@ def test_prefill_exact_integer(dsa, shape, topk):
 
 @pytest.mark.parametrize("shape,topk,cfg", [
     ((1, 256, 256, 4, 32), 16, 1),
-    ((1, 1000, 1000, 64, 128), 64, 2),     # many in-kernel compactions (capacity 192)
+    ((1, 1000, 1000, 64, 128), 64, 2),     # many in-kernel compactions (list capacity 576)
     ((1, 333, 333, 64, 64), 300, 3),       # k close to L
     ((1, 2, 2, 64, 128), 16, 4),           # smallest prefill
     ((1, 130, 700, 64, 128), 32, 5),       # chunked prefill: queries are the last 130 of 700
@@ -32,6 +32,25 @@ def test_prefill_random_bf16(dsa, shape, topk, cfg):
     say(f"prefill bf16 {shape} k={topk}")
     inp = make_indexer_inputs(*shape, config=cfg)
     check_indexer(dsa, inp, topk)
+
+
+@pytest.mark.parametrize("L", [63, 64, 65, 127, 128, 129, 191, 255, 257])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_prefill_tile_boundaries(dsa, L, dtype):
+    """Lengths around the 64-key sub-tile and 128-key iteration boundaries
+    (rows of one workgroup ending in different sub-tiles, a last sub-tile
+    wholly past the keys)."""
+    say(f"prefill {dtype} L={L}")
+    inp = make_indexer_inputs(1, L, L, 16, 64, config=11, dtype=dtype)
+    check_indexer(dsa, inp, 24)
+
+
+def test_prefill_small_k_many_shrinks(dsa):
+    """k = 8 over 3000 keys: the list (capacity k + 512) is shrunk over and over."""
+    say("prefill k=8 L=3000")
+    inp = make_indexer_inputs(1, 3000, 3000, 32, 64, config=12)
+    rows = [0, 7, 8, 519, 520, 521, 1500, 2999] + list(np.random.default_rng(1).choice(3000, 24, replace=False))
+    check_indexer(dsa, inp, 8, rows=sorted(set(int(r) for r in rows)))
 
 
 def test_prefill_k2048_compaction(dsa):
