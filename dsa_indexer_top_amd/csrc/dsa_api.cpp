@@ -230,22 +230,22 @@ void indexer_bind_workspace(IndexerParams& p, void* ws) {
 }
 
 int attn_nsplit(int B, int n_q, int topk) {
-  if (n_q > 1) return 1;
-  // decode: spread the requests' gathers over about 1024 waves, at least one
-  // 32-entry chunk per split and at most 64 splits (the merge uses one lane each)
+  // about 2048 waves over the whole call (the best measured from one decode
+  // request to 16K prefill rows), at least one 32-entry chunk per split, at
+  // most 64 splits; a power of two, so that from kAttnGroupWaves splits on
+  // they fill whole workgroups
+  const long rows = (long)B * n_q;
   const int chunks = (topk + 31) / 32;
-  int ns = 1024 / (B > 0 ? B : 1);
-  if (ns > chunks) ns = chunks;
-  if (ns > 64) ns = 64;
-  if (ns < 1) ns = 1;
+  int ns = 1;
+  while (ns < 64 && 2 * ns <= chunks && rows * 2 * ns <= 2048) ns *= 2;
   return ns;
 }
 
 size_t attn_workspace_bytes(int B, int n_q, int n_k, int H, int D, int topk) {
   (void)n_k;
-  const int ns = attn_nsplit(B, n_q, topk);
-  if (ns <= 1) return 0;
-  return round_up((size_t)B * n_q * ns * H * attn_part_stride(D) * 4, 256);
+  const int parts = attn_nparts(attn_nsplit(B, n_q, topk));
+  if (parts <= 1) return 0;
+  return round_up((size_t)B * n_q * parts * H * attn_part_stride(D) * 4, 256);
 }
 
 }  // namespace dsa

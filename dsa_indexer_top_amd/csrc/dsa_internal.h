@@ -98,8 +98,8 @@ struct AttnParams {
   const int32_t* idx;
   void* out;
   float* lse;
-  int nsplit;           // >1: split-K over the idx list (decode), partials in ws
-  float* part;          // [rows, nsplit, H, kAttnPartStride]: O[D], max, sum, pad
+  int nsplit;           // waves that share one row's idx list (split-K), attn_nsplit
+  float* part;          // [rows, attn_nparts(nsplit), H, kAttnPartStride]: O[D], max, sum, pad
   PagedKV kv;           // decode only: paged pools (kv.block_table) or flat
   void* const* ev;      // optional phase events (2): before, after
 };
@@ -113,6 +113,13 @@ inline int attn_part_stride(int D) { return D + 4; }
 size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk);
 size_t attn_workspace_bytes(int B, int n_q, int n_k, int H, int D, int topk);
 int attn_nsplit(int B, int n_q, int topk);
+// Waves per workgroup that merge their splits in LDS, and the partials per
+// row the merge kernel reads for nsplit splits: none for one split (the wave
+// writes the output), one per wave below kAttnGroupWaves splits, one per
+// workgroup of kAttnGroupWaves waves from there on (1 = written directly).
+constexpr int kAttnGroupWaves = 8;
+constexpr int kAttnMaxParts = 8;
+__host__ __device__ inline int attn_nparts(int nsplit) { return nsplit >= kAttnGroupWaves ? nsplit / kAttnGroupWaves : nsplit; }
 
 // Carves the workspace into the views above.
 void indexer_bind_workspace(IndexerParams& p, void* ws);

@@ -24,15 +24,26 @@
 // padded so the four lane groups of a read hit disjoint banks). Online
 // softmax in fp32 with exp2 (scale folded with log2 e); P is rounded to bf16
 // for the second product.
-// Decode (one query per request) splits the list over many waves; a second
-// kernel merges the per-split (O, max, sum) triples by the log-sum-exp rule.
+// Few rows (decode, short prefill chunks) split each row's list over several
+// waves (split-K) so that about 2048 waves share the call. Up to 4 splits
+// each wave writes its (O, max, sum) partial; from 8 splits on, the splits
+// of a workgroup of 8 waves are merged in LDS first, so a row has at most 8
+// partials, or none when one workgroup covers it. A second kernel merges a
+// row's partials by the log-sum-exp rule.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 4;  // waves per workgroup when every wave is on its own
 constexpr int kAttnChunk = 32;
+
+// Launch forms: one wave per row writing the output; one wave per split
+// writing a partial; workgroups of kAttnGroupWaves split waves that merge in
+// LDS and write the output (one workgroup per row) or one partial each.
+enum AttnMode { kAttnDirect = 0, kAttnSplit = 1, kAttnGroup = 2 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct AttnShape {
@@ -51,19 +62,27 @@ __device__ __forceinline__ int prow(int j) { return (j & 3) * 4 + (j >> 2); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(kAttnWaves * kWave) void sparse_attn_kernel(AttnParams p) {
+template <int D, int MODE, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void sparse_attn_kernel(AttnParams p) {
   using S = AttnShape<D>;
   static_assert((S::PSTRIDE / 4) % 64 == 16, "lane groups of a read must not share banks");
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v[kAttnWaves][16 * S::PSTRIDE];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v[WAVES][16 * S::PSTRIDE];
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
+  __builtin_assume(wave >= 0 && wave < WAVES);
   const int ns = p.nsplit;
-  const int rows = p.B * p.n_q;
-  const int wid = blockIdx.x * kAttnWaves + wave;
-  if (wid >= rows * ns) return;  // no workgroup barriers below
-  const int row = wid / ns;
-  const int split = wid - row * ns;
+  int row, split, wid;  // wid: this wave's (or workgroup's) partial
+  if constexpr (MODE == kAttnGroup) {
+    const int groups = ns / WAVES;  // workgroups per row
+    row = blockIdx.x / groups;
+    wid = blockIdx.x;
+    split = (blockIdx.x - row * groups) * WAVES + wave;
+  } else {
+    wid = blockIdx.x * WAVES + wave;
+    if (wid >= p.B * p.n_q * ns) return;  // no workgroup barriers in these forms
+    row = wid / ns;
+    split = wid - row * ns;
+  }
   const int b = row / p.n_q;
   const int t = row - b * p.n_q;
   const bool paged = p.kv.block_table != nullptr;  // decode over page pools (n_q == 1)
@@ -202,9 +221,65 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void sparse_attn_kernel(AttnPar
   // the four lane groups summed different keys of the same head
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
+  if constexpr (MODE == kAttnGroup) {
+    // each wave's (O, max, sum) into its own V buffer (its last reads of it
+    // are done: a wave's LDS operations execute in order) as O [16][D], the
+    // 16 maxima, the 16 sums; then the workgroup merges its WAVES splits per
+    // (head, dim) by the log-sum-exp rule
+    static_assert((16 * D + 32) * 4 <= 16 * S::PSTRIDE, "partial fits the V buffer");
+    float* mine = (float*)vl;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) *(f32x4*)(mine + i16 * D + 16 * db + 4 * g) = o[db];
+    if (g == 0) {
+      mine[16 * D + i16] = m;
+      mine[16 * D + 16 + i16] = l;
+    }
+    __syncthreads();
+    constexpr int DPT = 16 * D / (WAVES * kWave);  // dims per thread
+    constexpr int TPH = D / DPT;                   // threads per head
+    static_assert(DPT % 2 == 0 && DPT * WAVES * kWave == 16 * D, "merge layout");
+    const int h = threadIdx.x / TPH, d0 = (threadIdx.x % TPH) * DPT;
+    if (h >= p.H) return;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, ((const float*)lds_v[w])[16 * D + h]);
+    float L = 0.0f, acc[DPT];
+#pragma unroll
+    for (int c = 0; c < DPT; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float* pw = (const float*)lds_v[w];
+      const float mw = pw[16 * D + h];
+      const float f = mw == -__builtin_inff() ? 0.0f : exp2_fast(mw - M);
+      L = __builtin_fmaf(pw[16 * D + 16 + h], f, L);
+#pragma unroll
+      for (int c = 0; c < DPT; c += 2) {
+        const f32x2 x = *(const f32x2*)(pw + h * D + d0 + c);
+        acc[c] = __builtin_fmaf(f, x[0], acc[c]);
+        acc[c + 1] = __builtin_fmaf(f, x[1], acc[c + 1]);
+      }
+    }
+    if (ns > WAVES) {  // one partial per workgroup, merged by attn_combine_kernel
+      float* dst = p.part + ((size_t)wid * p.H + h) * kAttnPartStride<D>;
+#pragma unroll
+      for (int c = 0; c < DPT; c += 2) *(f32x2*)(dst + d0 + c) = (f32x2){acc[c], acc[c + 1]};
+      if (d0 == 0) {
+        dst[D] = M;
+        dst[D + 1] = L;
+      }
+      return;
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    __bf16* dst = (__bf16*)p.out + ((size_t)row * p.H + h) * D + d0;
+#pragma unroll
+    for (int c = 0; c < DPT; ++c) dst[c] = (__bf16)(acc[c] * inv);
+    if (p.lse && d0 == 0)
+      p.lse[(size_t)row * p.H + h] = L > 0.0f ? (M + __log2f(L)) * 0.6931471805599453f : -__builtin_inff();
+    return;
+  }
   if (i16 >= p.H) return;
   // lane holds O[head i16][16*db + 4*g + r]
-  if constexpr (SPLIT) {
+  if constexpr (MODE == kAttnSplit) {
     float* dst = p.part + ((size_t)wid * p.H + i16) * kAttnPartStride<D>;
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) *(f32x4*)(dst + 16 * db + 4 * g) = o[db];
@@ -228,9 +303,9 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void sparse_attn_kernel(AttnPar
   }
 }
 
-// Merges the split partials of one (query, head) per wave:
+// Merges the partials of one (query, head) per wave:
 // M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s o_s 2^(m_s - M) / L
-// (m in log2 units; splits with no valid entry have m = -inf, l = 0, o = 0).
+// (m in log2 units; a partial with no valid entry has m = -inf, l = 0, o = 0).
 template <int D, int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   constexpr int DPL = D / kWave;  // output dims per lane
@@ -238,7 +313,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int row = blockIdx.y;
   if (h >= p.H) return;
-  const int ns = p.nsplit;  // <= NS <= 64
+  const int ns = attn_nparts(p.nsplit);  // <= NS
   const size_t sstride = (size_t)p.H * kAttnPartStride<D>;
   const float* base = p.part + ((size_t)row * ns * p.H + h) * kAttnPartStride<D>;
   // every split's partial O first (independent of the weights), then m and l,
@@ -278,19 +353,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 template <int D>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s) {
   const int rows = p.B * p.n_q;
-  const long waves = (long)rows * p.nsplit;
-  const dim3 grid((unsigned)((waves + kAttnWaves - 1) / kAttnWaves));
-  if (p.nsplit > 1) {
-    hipLaunchKernelGGL((sparse_attn_kernel<D, true>), grid, dim3(kAttnWaves * kWave), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (p.nsplit <= 32)
-      hipLaunchKernelGGL((attn_combine_kernel<D, 32>), dim3((p.H + 3) / 4, rows), dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((attn_combine_kernel<D, 64>), dim3((p.H + 3) / 4, rows), dim3(256), 0, s, p);
-  } else {
-    hipLaunchKernelGGL((sparse_attn_kernel<D, false>), grid, dim3(kAttnWaves * kWave), 0, s, p);
-  }
+  const int ns = p.nsplit;
+  if (ns < 1 || ns > 64 || (ns >= kAttnGroupWaves && ns % kAttnGroupWaves) || attn_nparts(ns) > kAttnMaxParts)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(((long)rows * ns + kAttnWaves - 1) / kAttnWaves));
+  if (ns >= kAttnGroupWaves)
+    hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnGroup, kAttnGroupWaves>), dim3(rows * (ns / kAttnGroupWaves)),
+                       dim3(kAttnGroupWaves * kWave), 0, s, p);
+  else if (ns > 1)
+    hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnSplit, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
+  else
+    hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnDirect, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || attn_nparts(ns) <= 1) return e;
+  hipLaunchKernelGGL((attn_combine_kernel<D, kAttnMaxParts>), dim3((p.H + 3) / 4, rows), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

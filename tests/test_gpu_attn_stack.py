@@ -78,6 +78,21 @@ def test_attn_decode_split(dsa, B, n_k, topk):
     _check_attn(dsa, a, _random_idx(B, 1, n_k, topk, n_k - 1, 2))
 
 
+@pytest.mark.parametrize("B,n_q,n_k,H,D,topk", [
+    (1, 2048, 2048, 4, 64, 64),       # one wave per row, two chunks
+    (1, 256, 2000, 16, 128, 512),     # 8 splits: one workgroup per row merges in LDS
+    (1, 128, 3000, 12, 64, 700),      # 16 splits: two workgroup partials, ragged last chunk
+    (4, 16, 5000, 16, 128, 1500),     # 32 splits: four workgroup partials, empty last splits
+    (1, 1, 5000, 5, 64, 2048),        # 64 splits, D = 64, 5 heads
+])
+def test_attn_split_forms(dsa, B, n_q, n_k, H, D, topk):
+    """Each launch form of the split-K rule (about 2048 waves per call): direct,
+    per-wave partials, and 8-wave workgroups merging in LDS with 1..8 partials."""
+    say(f"attn forms B={B} n_q={n_q} n_k={n_k} H={H} D={D} k={topk}")
+    a = make_attn_inputs(B, n_q, n_k, H, D, config=34)
+    _check_attn(dsa, a, _random_idx(B, n_q, n_k, topk, n_k - n_q, 3, junk=True))
+
+
 # ------------------------------------------------------------------ stack
 def _stack_layers(n_layers, L, H_I, D_I, H, D, config, dtype="bf16"):
     dev, host = [], []
