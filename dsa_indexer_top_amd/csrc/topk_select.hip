@@ -17,26 +17,22 @@ namespace dsa {
 constexpr int kFinNTPrefill = 512;
 constexpr int kFinNTDecode = 512;
 
-// Block-wide exclusive prefix sum of one value per thread (blockDim.x <= 1024).
-__device__ int block_excl_scan(int v, int* scratch /* >= 17 ints */, int* total) {
+// Block-wide exclusive prefix sum of one value per thread (blockDim.x <= 1024):
+// each wave posts its total, then every wave adds up the totals before it.
+__device__ int block_excl_scan(int v, int* scratch /* >= 16 ints */, int* total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const uint32_t incl = wave_incl_scan((uint32_t)v);
   if (lane == 63) scratch[wave] = (int)incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int x = scratch[w];
-      scratch[w] = acc;
-      acc += x;
-    }
-    scratch[16] = acc;
+  int before = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int x = scratch[w];
+    before += w < wave ? x : 0;
+    all += x;
   }
-  __syncthreads();
-  const int r = scratch[wave] + (int)incl - v;
-  *total = scratch[16];
-  __syncthreads();
-  return r;
+  *total = all;
+  __syncthreads();  // scratch is free for the next call
+  return before + (int)incl - v;
 }
 
 // The k-th largest of the keys of the participating entries i < n (get(i, u)
@@ -278,8 +274,159 @@ __global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(Finaliz
   write_sorted(p, r, wkey, widx, take);
 }
 
+// Exact top-k of an unordered decode candidate list (1 <= cnt <= kMaxC
+// entries, distinct indices, a superset of the top-k) by ranking instead of
+// sorting. Entries go to 2^kBucketBits buckets by the top bits of (max key -
+// key), so that every entry of a lower bucket has a larger key; an LDS
+// counting pass returns each entry's slot in its bucket, an exclusive scan of
+// the counts gives each bucket's first rank, and each entry's 64-bit order
+// word (key, ~index) is stored at its slot. An entry's rank is its bucket's
+// first rank plus the members of its bucket with a larger order word (larger
+// key, or equal key and lower index); entries ranked below `take` are written
+// straight to their output slots. If a bucket holds more than kBucketMaxRun
+// entries (heavy ties), it returns false before writing any output.
+constexpr int kBucketBits = 12;
+constexpr int kBuckets = 1 << kBucketBits;
+constexpr int kBucketPer = kMaxC / kFinNTDecode;  // entries per thread
+constexpr int kBucketEarly = kBucketPer / 2;      // of them loaded before the count is known
+constexpr int kBucketMaxRun = 256;
+constexpr int kBucketLdsBytes = kMaxC * 8 + kBuckets * 4;
+
+// Entry i = threadIdx.x + e * kFinNTDecode of the list (entries past the
+// list's end are ignored).
+struct BucketEntries {
+  uint32_t u[kBucketPer];
+  int32_t x[kBucketPer];
+};
+
+__device__ void bucket_load(BucketEntries& v, const uint32_t* __restrict__ ck, const int32_t* __restrict__ ci,
+                            int e0, int e1, int lim) {
+#pragma unroll
+  for (int e = 0; e < kBucketPer; ++e) {
+    if (e < e0 || e >= e1) continue;
+    const int i = threadIdx.x + e * kFinNTDecode;
+    v.u[e] = i < lim ? ck[i] : 0u;
+    v.x[e] = i < lim ? ci[i] : 0;
+  }
+}
+
+__device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEntries& v, int cnt, int take,
+                                 uint64_t* word, uint32_t* base, int* scratch) {
+  constexpr int PER = kBucketPer, BPT = kBuckets / kFinNTDecode;  // buckets per thread
+  static_assert(BPT * kFinNTDecode == kBuckets && PER * kFinNTDecode == kMaxC, "bucket layout");
+  __shared__ uint32_t sh_min[kSortWaves], sh_max[kSortWaves], sh_run[kSortWaves];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (threadIdx.x + e * kFinNTDecode < cnt) {
+      mn = min(mn, v.u[e]);
+      mx = max(mx, v.u[e]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) base[BPT * threadIdx.x + q] = 0u;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+  }
+  if (lane == 0) {
+    sh_min[w] = mn;
+    sh_max[w] = mx;
+  }
+  __syncthreads();
+  uint32_t umin = sh_min[0], umax = sh_max[0];
+#pragma unroll
+  for (int q = 1; q < kSortWaves; ++q) {
+    umin = min(umin, sh_min[q]);
+    umax = max(umax, sh_max[q]);
+  }
+  const uint32_t range = umax - umin;
+  const int shift = (range >> kBucketBits) ? 32 - __builtin_clz(range) - kBucketBits : 0;  // range >> shift < kBuckets
+  uint32_t slot[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    slot[e] = threadIdx.x + e * kFinNTDecode < cnt ? atomicAdd(&base[(umax - v.u[e]) >> shift], 1u) : 0u;
+  __syncthreads();
+  uint32_t c[BPT], local = 0u, run = 0u;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    c[q] = base[BPT * threadIdx.x + q];
+    local += c[q];
+    run = max(run, c[q]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) run = max(run, (uint32_t)__shfl_xor((int)run, d, 64));
+  if (lane == 0) sh_run[w] = run;
+  int total;
+  uint32_t pre = (uint32_t)block_excl_scan((int)local, scratch, &total);  // its barriers order the reads above
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    base[BPT * threadIdx.x + q] = pre;
+    pre += c[q];
+  }
+  int max_run = (int)sh_run[0];
+#pragma unroll
+  for (int q = 1; q < kSortWaves; ++q) max_run = max(max_run, (int)sh_run[q]);  // uniform
+  __syncthreads();
+  if (max_run > kBucketMaxRun) return false;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (threadIdx.x + e * kFinNTDecode < cnt)
+      word[base[(umax - v.u[e]) >> shift] + slot[e]] = ((uint64_t)v.u[e] << 32) | (uint32_t)~(uint32_t)v.x[e];
+  __syncthreads();
+  int32_t* oi = p.out_idx + (size_t)r * p.topk;
+  float* os = p.out_scores ? p.out_scores + (size_t)r * p.topk : nullptr;
+  // in two halves, all entries of a half step through their buckets together
+  // with no branch between the reads, so that the reads are in flight at once
+  // (a step past an entry's bucket re-reads its last member, not counted)
+  constexpr int H = PER / 2;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint64_t mine[H];
+    int s0[H], rank[H], last[H], len[H], wrun = 0;
+#pragma unroll
+    for (int q = 0; q < H; ++q) {
+      const int e = h * H + q;
+      const bool in = threadIdx.x + e * kFinNTDecode < cnt;
+      const uint32_t bk = in ? (umax - v.u[e]) >> shift : 0u;
+      s0[q] = (int)base[bk];
+      len[q] = in ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : cnt) - s0[q] : 0;
+      mine[q] = ((uint64_t)v.u[e] << 32) | (uint32_t)~(uint32_t)v.x[e];
+      rank[q] = s0[q];
+      last[q] = s0[q] + max(len[q] - 1, 0);
+      wrun = max(wrun, len[q]);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) wrun = max(wrun, __shfl_xor(wrun, d, 64));
+    wrun = uniform_i(wrun);
+    for (int j = 0; j < wrun; ++j) {
+      uint64_t o[H];
+#pragma unroll
+      for (int q = 0; q < H; ++q) o[q] = word[min(s0[q] + j, last[q])];
+#pragma unroll
+      for (int q = 0; q < H; ++q) rank[q] += (int)(o[q] > mine[q]) & (int)(j < len[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < H; ++q) {
+      const int e = h * H + q;
+      if (len[q] > 0 && rank[q] < take) {  // len > 0: a listed entry (its bucket holds at least itself)
+        oi[rank[q]] = v.x[e];
+        if (os) os[rank[q]] = key_score(v.u[e]);
+      }
+    }
+  }
+  for (int i = take + (int)threadIdx.x; i < p.topk; i += blockDim.x) {
+    oi[i] = -1;
+    if (os) os[i] = -__builtin_inff();
+  }
+  return true;
+}
+
 // Decode requests: the candidate list is unordered (<= C entries, a superset
-// of the top-k). The k-th key theta is found in LDS; if more entries tie at
+// of the top-k). Lists without heavy ties are ranked by bucket_rank_topk;
+// otherwise the k-th key theta is found in LDS; if more entries tie at
 // theta than the top-k takes, a second select over their inverted indices
 // keeps the lowest ones. The winners (in list order) are radix-sorted by key,
 // then each run of equal keys is put in index order (a run longer than 32:
@@ -289,25 +436,36 @@ __global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(Finaliz
 __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeParams p) {
   static_assert(kFinNTDecode == kSortWaves * kWave && kSortN >= kMaxTopk, "sort layout");
   static_assert(kMaxC >= 2 * kSortN + 256 * kSortWaves, "sort scratch must fit in skey");
-  __shared__ uint32_t skey[kMaxC];
-  __shared__ uint32_t wkey[kSortN];
-  __shared__ int32_t widx[kSortN];
+  // one LDS buffer: the bucket path's order words and bucket counts, or the
+  // sort path's candidate keys (skey) and winners (wkey, widx)
+  static_assert(kMaxC * 4 + 2 * kSortN * 4 <= kBucketLdsBytes, "sort path fits the buffer");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kBucketLdsBytes];
+  uint32_t* const skey = (uint32_t*)lds;
+  uint32_t* const wkey = skey + kMaxC;
+  int32_t* const widx = (int32_t*)(wkey + kSortN);
   __shared__ uint32_t hist[256];
   __shared__ int scratch[17];
   __shared__ int sh_n;
   const int r = blockIdx.x;  // n_q == 1: row = request
   const int n_valid = decode_len(p.kv, r, p.pos_offset, p.n_k);
   const int k_eff = min(p.topk, n_valid);
+  const uint32_t* ck = p.cand_key + (size_t)r * p.C;
+  const int32_t* ci = p.cand_idx + (size_t)r * p.C;
+  // the list's first entries are loaded together with its count
+  BucketEntries ent;
+  bucket_load(ent, ck, ci, 0, kBucketEarly, min(p.C, kMaxC));
   const int cnt = p.cand_cnt[r];
   int take;
   bool ordered;  // winners already in index order
   if (cnt <= p.C) {
-    const uint32_t* ck = p.cand_key + (size_t)r * p.C;
-    const int32_t* ci = p.cand_idx + (size_t)r * p.C;
+    take = min(k_eff, cnt);  // cnt >= k_eff by construction
+    if (cnt >= 1) {
+      bucket_load(ent, ck, ci, kBucketEarly, kBucketPer, cnt);  // the rest (zeros past the end)
+      if (bucket_rank_topk(p, r, ent, cnt, take, (uint64_t*)lds, (uint32_t*)(lds + kMaxC * 8), scratch)) return;
+    }
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
     if (threadIdx.x == 0) sh_n = 0;
     __syncthreads();
-    take = min(k_eff, cnt);  // cnt >= k_eff by construction
     uint32_t theta = 0u;     // below every finite score's key: keep all
     uint32_t cut = 0u;       // keep ties with ~index >= cut
     if (cnt > take) {

@@ -143,6 +143,33 @@ def test_decode_all_ties_overflow_path(dsa):
     assert r.idx.cpu().numpy()[0, 0].tolist() == list(range(2048))
 
 
+def test_decode_dense_threshold_bin(dsa):
+    """Every key in one 12-bit histogram bin, so the candidate list holds all
+    6000 keys (more than half its 8192-entry capacity): the ranking path with
+    its second batch of entries, nearly all scores distinct."""
+    say("decode dense bin")
+    inp = make_indexer_inputs(2, 1, 6000, 16, 128, config=25)
+    g = torch.Generator().manual_seed(5)
+    # scores 11.5 +- 0.1: inside [11, 12), one bin of the top 12 order-key bits
+    inp.k.copy_((1.0 + 0.02 * torch.randn(inp.k.shape, generator=g)).to(inp.k.dtype))
+    inp.q.copy_((0.0898 + 0.002 * torch.randn(inp.q.shape, generator=g)).to(inp.q.dtype))
+    inp.w.fill_(1.0 / 16)
+    r, _ = check_indexer(dsa, inp, 2048)
+    full = r.full_scores.cpu().numpy()
+    assert np.all(full > 11.0) and np.all(full < 12.0)
+
+
+def test_decode_all_ties_within_capacity(dsa):
+    """All 6000 scores equal with the list inside its capacity: one bucket
+    exceeds the ranking path's run limit and the sort path takes over; the
+    tie rule gives the first k indices."""
+    say("decode all ties, list within capacity")
+    inp = make_indexer_inputs(1, 1, 6000, 64, 128, config=26)
+    inp.q.zero_()
+    r, _ = check_indexer(dsa, inp, 2048, exact=True)
+    assert r.idx.cpu().numpy()[0, 0].tolist() == list(range(2048))
+
+
 def test_decode_fp8(dsa):
     say("decode fp8")
     inp = make_indexer_inputs(2, 1, 4000, 64, 128, config=24, dtype="fp8")
