@@ -204,9 +204,10 @@ size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk) {
   if (n_q == 1) {
     sz += (size_t)B * decode_key_stride(n_k) * 4;                    // decode keys
     sz += round_up(((size_t)B + kDecodeTargetBlocks) * 3 * 4, 256);  // ragged-decode block plan
-    sz += (size_t)B * kDecodeHistStride * 4;  // decode histograms (a multiple of 256 B) ...
+    sz += (size_t)B * kDecodeHistStride * 4;  // decode histograms and counters
+  } else {
+    sz += round_up(rows * 4, 256);  // cand_cnt
   }
-  sz += round_up(rows * 4, 256);  // ... directly followed by cand_cnt
   return sz;
 }
 
@@ -224,9 +225,12 @@ void indexer_bind_workspace(IndexerParams& p, void* ws) {
     p.dec_work = (int32_t*)c;
     c += round_up(((size_t)p.B + kDecodeTargetBlocks) * 3 * 4, 256);
     p.dec_hist = (uint32_t*)c;
-    c += (size_t)p.B * kDecodeHistStride * 4;
+    p.cand_cnt = (int32_t*)(p.dec_hist + kDecodeCntOffset);
+    p.cnt_stride = kDecodeHistStride;
+  } else {
+    p.cand_cnt = (int32_t*)c;
+    p.cnt_stride = 1;
   }
-  p.cand_cnt = (int32_t*)c;
 }
 
 int attn_nsplit(int B, int n_q, int topk) {

@@ -26,7 +26,11 @@ inline int cand_capacity(int topk, bool decode) {
 constexpr int kDecodeHistBits = 12;
 constexpr int kDecodeHistBins = 1 << kDecodeHistBits;
 constexpr int kDecodeCoarseBins = 64;  // sums of 64 consecutive bins, stored after them
-constexpr int kDecodeHistStride = kDecodeHistBins + kDecodeCoarseBins;
+// Each request's row: the fine bins, the coarse bins, then its candidate
+// counter alone in the last 256 bytes (the requests' counters sit a row
+// apart, so the collect blocks' atomics on them do not queue on one line).
+constexpr int kDecodeCntOffset = kDecodeHistBins + kDecodeCoarseBins;
+constexpr int kDecodeHistStride = kDecodeCntOffset + 64;
 // Row stride of the decode score keys: n_k rounded up to 64 keys (256 B), so
 // every row starts aligned and 16-key vector reads stay inside it.
 __host__ __device__ inline size_t decode_key_stride(int n_k) { return ((size_t)n_k + 63) / 64 * 64; }
@@ -73,11 +77,11 @@ struct IndexerParams {
   // workspace views
   uint32_t* cand_key;   // [rows, C]
   int32_t* cand_idx;    // [rows, C]
-  int32_t* cand_cnt;    // [rows]
+  int32_t* cand_cnt;    // [rows], row r at cand_cnt[r * cnt_stride]
+  int cnt_stride;       // 1 (prefill) or kDecodeHistStride (decode: inside the histogram rows)
   int C;
   uint32_t* dec_keys;   // decode: [B, dec_stride] score keys
-  uint32_t* dec_hist;   // decode: [B, kDecodeHistStride] (fine bins, then coarse bins),
-                        // directly followed by cand_cnt (one fill zeroes both)
+  uint32_t* dec_hist;   // decode: [B, kDecodeHistStride] (fine bins, coarse bins, counter)
   int32_t* dec_work;    // decode: [B + kDecodeTargetBlocks, 3] (request, k0, k1) per score
                         // block, planned on the device when lengths are ragged (kv.seq_lens)
   PagedKV kv;           // decode only: paged pools (kv.block_table) or flat

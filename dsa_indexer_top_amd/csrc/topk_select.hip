@@ -211,7 +211,8 @@ struct FinalizeParams {
   int rows, C, topk, n_q, n_k, pos_offset;
   const uint32_t* cand_key;
   const int32_t* cand_idx;
-  const int32_t* cand_cnt;
+  const int32_t* cand_cnt;  // row r at cand_cnt[r * cnt_stride]
+  int cnt_stride;
   const uint32_t* full_keys;  // decode: [rows, decode_key_stride(n_k)] keys for the overflow path
   PagedKV kv;                 // decode: per-request lengths (kv.seq_lens) or none
   int32_t* out_idx;
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(Finaliz
   const int t = r % p.n_q;
   const int n_valid = min(p.pos_offset + t + 1, p.n_k);
   const int k_eff = min(p.topk, n_valid);
-  const int cnt = min(p.cand_cnt[r], p.C);  // >= k_eff by construction
+  const int cnt = min(p.cand_cnt[(size_t)r * p.cnt_stride], p.C);  // >= k_eff by construction
   const uint32_t* ck = p.cand_key + (size_t)r * p.C;
   const int32_t* ci = p.cand_idx + (size_t)r * p.C;
   for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
   // the list's first entries are loaded together with its count
   BucketEntries ent;
   bucket_load(ent, ck, ci, 0, kBucketEarly, min(p.C, kMaxC));
-  const int cnt = p.cand_cnt[r];
+  const int cnt = p.cand_cnt[(size_t)r * p.cnt_stride];
   int take;
   bool ordered;  // winners already in index order
   if (cnt <= p.C) {
@@ -562,6 +563,7 @@ hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s
   p.cand_key = ip.cand_key;
   p.cand_idx = ip.cand_idx;
   p.cand_cnt = ip.cand_cnt;
+  p.cnt_stride = ip.cnt_stride;
   p.full_keys = ip.dec_keys;
   p.kv = ip.kv;
   p.out_idx = ip.out_idx;
@@ -887,7 +889,7 @@ __global__ __launch_bounds__(256) void decode_collect_kernel(IndexerParams p) {
   int total;
   int pos = block_excl_scan(n, scratch, &total);
   if (total == 0) return;
-  if (threadIdx.x == 0) sh_base = atomicAdd(&p.cand_cnt[b], total);
+  if (threadIdx.x == 0) sh_base = atomicAdd(&p.cand_cnt[(size_t)b * p.cnt_stride], total);
   __syncthreads();
   pos += sh_base;
   uint32_t* ck = p.cand_key + (size_t)b * p.C;
@@ -926,9 +928,9 @@ static void launch_decode_scores_t(const IndexerParams& p, hipStream_t s) {
 }
 
 hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
-  // zero the histograms and the counters that follow them (a kernel, not a
-  // memset node), and plan ragged score blocks
-  const size_t nz = (size_t)p.B * kDecodeHistStride + (size_t)p.B;
+  // zero the histograms and counters (a kernel, not a memset node), and plan
+  // ragged score blocks
+  const size_t nz = (size_t)p.B * kDecodeHistStride;
   hipLaunchKernelGGL(decode_prepare_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 1024)), dim3(256), 0,
                      s, p, nz, p.B + kDecodeTargetBlocks);
   hipError_t e = record_phase(p.ev, 0, s);
