@@ -54,12 +54,13 @@ def test_prefill_small_k_many_shrinks(dsa):
 
 
 def test_prefill_k2048_compaction(dsa):
-    """k = 2048 with rows longer than the 4096-entry candidate list, so the exact
-    in-kernel compaction runs; sampled rows incl. the first compacting ones."""
-    L = 4700
+    """k = 2048 with rows longer than the 8192-entry candidate list (4k), so the
+    in-kernel shrink runs (first when a list nears 8192 - 256 entries); sampled
+    rows incl. the first shrinking ones and the capacity boundary."""
+    L = 9000
     say(f"prefill bf16 L={L} k=2048")
     inp = make_indexer_inputs(1, L, L, 64, 128, config=6, w_std=0.125)
-    rows = [0, 1, 2046, 2047, 2048, 2049, 4030, 4031, 4032, 4033, 4095, 4096, 4200, L - 2, L - 1]
+    rows = [0, 1, 2046, 2047, 2048, 2049, 7870, 7935, 7936, 7937, 8000, 8191, 8192, 8193, L - 2, L - 1]
     rows += list(np.random.default_rng(0).choice(L, 25, replace=False))
     check_indexer(dsa, inp, 2048, rows=sorted(set(int(r) for r in rows)))
 
