@@ -232,48 +232,11 @@ __device__ void write_sorted(const FinalizeParams& p, int r, const uint32_t* wke
 }
 
 // Prefill rows: each candidate list (<= kMaxC entries, in index order)
-// is a superset of the row's top-k. The exact k-th key is found in LDS, the k
-// winners are collected in list order (ties: lowest index) and sorted.
+// is a superset of the row's top-k. Lists without heavy ties are ranked by
+// bucket_rank_topk (below); otherwise the exact k-th key is found in LDS, the
+// k winners are collected in list order (ties: lowest index) and sorted.
 constexpr int kMaxC = 8192;
 constexpr int kMaxTopk = 2048;
-
-__global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(FinalizeParams p) {
-  static_assert(kFinNTPrefill == kSortWaves * kWave && kSortN >= kMaxTopk, "sort layout");
-  // skey: the candidate keys; after the collect, the sort's second buffers
-  // and its histograms
-  __shared__ uint32_t skey[kMaxC];
-  __shared__ uint32_t wkey[kSortN];
-  __shared__ int32_t widx[kSortN];
-  __shared__ uint32_t hist[256];
-  __shared__ int scratch[17];
-  static_assert(kMaxC >= 2 * kSortN + 256 * kSortWaves, "sort scratch must fit in skey");
-  const int r = blockIdx.x;
-  const int t = r % p.n_q;
-  const int n_valid = min(p.pos_offset + t + 1, p.n_k);
-  const int k_eff = min(p.topk, n_valid);
-  const int cnt = min(p.cand_cnt[(size_t)r * p.cnt_stride], p.C);  // >= k_eff by construction
-  const uint32_t* ck = p.cand_key + (size_t)r * p.C;
-  const int32_t* ci = p.cand_idx + (size_t)r * p.C;
-  for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
-  __syncthreads();
-  uint32_t theta = 0u;
-  int need = 1 << 30;
-  const int take = min(k_eff, cnt);
-  if (cnt > take) block_kth_key(skey, cnt, take, hist, &theta, &need);
-  // winners in list order, i.e. index order; padding (key 0) sorts last
-  block_ordered_emit(skey, ci, cnt, theta, need, scratch, [&](int pos, uint32_t u, int32_t ix) {
-    wkey[pos] = u;
-    widx[pos] = ix;
-  });
-  for (int i = take + (int)threadIdx.x; i < kSortN; i += blockDim.x) {
-    wkey[i] = 0u;
-    widx[i] = -1;
-  }
-  __syncthreads();
-  // stable by key: equal keys stay in index order, the tie rule
-  block_radix_sort_desc(wkey, widx, skey, (int32_t*)(skey + kSortN), skey + 2 * kSortN, scratch);
-  write_sorted(p, r, wkey, widx, take);
-}
 
 // Exact top-k of an unordered decode candidate list (1 <= cnt <= kMaxC
 // entries, distinct indices, a superset of the top-k) by ranking instead of
@@ -286,12 +249,12 @@ __global__ __launch_bounds__(kFinNTPrefill) void prefill_finalize_kernel(Finaliz
 // key, or equal key and lower index); entries ranked below `take` are written
 // straight to their output slots. If a bucket holds more than kBucketMaxRun
 // entries (heavy ties), it returns false before writing any output.
-constexpr int kBucketBits = 12;
-constexpr int kBuckets = 1 << kBucketBits;
+static_assert(kFinNTPrefill == kFinNTDecode, "one bucket layout for both finalize kernels");
 constexpr int kBucketPer = kMaxC / kFinNTDecode;  // entries per thread
 constexpr int kBucketEarly = kBucketPer / 2;      // of them loaded before the count is known
 constexpr int kBucketMaxRun = 256;
-constexpr int kBucketLdsBytes = kMaxC * 8 + kBuckets * 4;
+// LDS of the ranking path: the order words, then the bucket counts
+constexpr int bucket_lds_bytes(int bits) { return kMaxC * 8 + (4 << bits); }
 
 // Entry i = threadIdx.x + e * kFinNTDecode of the list (entries past the
 // list's end are ignored).
@@ -311,8 +274,10 @@ __device__ void bucket_load(BucketEntries& v, const uint32_t* __restrict__ ck, c
   }
 }
 
+template <int kBucketBits, int H>
 __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEntries& v, int cnt, int take,
                                  uint64_t* word, uint32_t* base, int* scratch) {
+  constexpr int kBuckets = 1 << kBucketBits;
   constexpr int PER = kBucketPer, BPT = kBuckets / kFinNTDecode;  // buckets per thread
   static_assert(BPT * kFinNTDecode == kBuckets && PER * kFinNTDecode == kMaxC, "bucket layout");
   __shared__ uint32_t sh_min[kSortWaves], sh_max[kSortWaves], sh_run[kSortWaves];
@@ -362,9 +327,13 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
   if (lane == 0) sh_run[w] = run;
   int total;
   uint32_t pre = (uint32_t)block_excl_scan((int)local, scratch, &total);  // its barriers order the reads above
+  // buckets are laid out in rank order, so the entries that can rank below
+  // `take` are the prefix up to the end of the bucket holding rank take - 1
+  __shared__ int sh_prefix;
 #pragma unroll
   for (int q = 0; q < BPT; ++q) {
     base[BPT * threadIdx.x + q] = pre;
+    if (c[q] && pre <= (uint32_t)(take - 1) && (uint32_t)(take - 1) < pre + c[q]) sh_prefix = (int)(pre + c[q]);
     pre += c[q];
   }
   int max_run = (int)sh_run[0];
@@ -372,29 +341,33 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
   for (int q = 1; q < kSortWaves; ++q) max_run = max(max_run, (int)sh_run[q]);  // uniform
   __syncthreads();
   if (max_run > kBucketMaxRun) return false;
+  const int prefix = sh_prefix;  // take <= cnt, so one bucket holds rank take - 1
 #pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (threadIdx.x + e * kFinNTDecode < cnt)
-      word[base[(umax - v.u[e]) >> shift] + slot[e]] = ((uint64_t)v.u[e] << 32) | (uint32_t)~(uint32_t)v.x[e];
+  for (int e = 0; e < PER; ++e) {
+    if (threadIdx.x + e * kFinNTDecode < cnt) {
+      const int s0 = (int)base[(umax - v.u[e]) >> shift];
+      if (s0 < prefix) word[s0 + slot[e]] = ((uint64_t)v.u[e] << 32) | (uint32_t)~(uint32_t)v.x[e];
+    }
+  }
   __syncthreads();
   int32_t* oi = p.out_idx + (size_t)r * p.topk;
   float* os = p.out_scores ? p.out_scores + (size_t)r * p.topk : nullptr;
-  // in two halves, all entries of a half step through their buckets together
-  // with no branch between the reads, so that the reads are in flight at once
-  // (a step past an entry's bucket re-reads its last member, not counted)
-  constexpr int H = PER / 2;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  // positions j < prefix of the bucket-ordered words, consecutive positions on
+  // consecutive lanes (so a wave's lanes mostly share a bucket), H per thread
+  // at a time: each steps through its bucket with no branch between the LDS
+  // reads, so that they are in flight together (a step past the bucket
+  // re-reads its last member and is not counted)
+  for (int g0 = 0; g0 * kFinNTDecode < prefix; g0 += H) {
     uint64_t mine[H];
     int s0[H], rank[H], last[H], len[H], wrun = 0;
 #pragma unroll
     for (int q = 0; q < H; ++q) {
-      const int e = h * H + q;
-      const bool in = threadIdx.x + e * kFinNTDecode < cnt;
-      const uint32_t bk = in ? (umax - v.u[e]) >> shift : 0u;
-      s0[q] = (int)base[bk];
+      const int j = threadIdx.x + (g0 + q) * kFinNTDecode;
+      const bool in = j < prefix;
+      mine[q] = word[in ? j : 0];
+      const uint32_t bk = (umax - (uint32_t)(mine[q] >> 32)) >> shift;
+      s0[q] = (int)base[in ? bk : 0u];
       len[q] = in ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : cnt) - s0[q] : 0;
-      mine[q] = ((uint64_t)v.u[e] << 32) | (uint32_t)~(uint32_t)v.x[e];
       rank[q] = s0[q];
       last[q] = s0[q] + max(len[q] - 1, 0);
       wrun = max(wrun, len[q]);
@@ -411,10 +384,9 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
     }
 #pragma unroll
     for (int q = 0; q < H; ++q) {
-      const int e = h * H + q;
-      if (len[q] > 0 && rank[q] < take) {  // len > 0: a listed entry (its bucket holds at least itself)
-        oi[rank[q]] = v.x[e];
-        if (os) os[rank[q]] = key_score(v.u[e]);
+      if (len[q] > 0 && rank[q] < take) {  // len > 0: a position below the prefix
+        oi[rank[q]] = (int32_t)~(uint32_t)mine[q];
+        if (os) os[rank[q]] = key_score((uint32_t)(mine[q] >> 32));
       }
     }
   }
@@ -423,6 +395,59 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
     if (os) os[i] = -__builtin_inff();
   }
   return true;
+}
+
+// two workgroups per CU (4 waves per SIMD: at most 128 VGPRs), so one row's
+// barriers and loads overlap another's work
+__global__ __launch_bounds__(kFinNTPrefill) __attribute__((amdgpu_waves_per_eu(4))) void prefill_finalize_kernel(
+    FinalizeParams p) {
+  static_assert(kFinNTPrefill == kSortWaves * kWave && kSortN >= kMaxTopk, "sort layout");
+  static_assert(kMaxC >= 2 * kSortN + 256 * kSortWaves, "sort scratch must fit in skey");
+  // one LDS buffer (72 KB: two workgroups per CU): the ranking path's words and
+  // bucket counts, or the sort path's candidate keys (skey; after the collect,
+  // the sort's second buffers and histograms), winners (wkey, widx) and the
+  // select histogram
+  constexpr int kBits = 11;
+  static_assert(kMaxC * 4 + 2 * kSortN * 4 + 256 * 4 <= bucket_lds_bytes(kBits), "sort path fits the buffer");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[bucket_lds_bytes(kBits)];
+  uint32_t* const skey = (uint32_t*)lds;
+  uint32_t* const wkey = skey + kMaxC;
+  int32_t* const widx = (int32_t*)(wkey + kSortN);
+  uint32_t* const hist = (uint32_t*)(widx + kSortN);
+  __shared__ int scratch[17];
+  const int r = blockIdx.x;
+  const int t = r % p.n_q;
+  const int n_valid = min(p.pos_offset + t + 1, p.n_k);
+  const int k_eff = min(p.topk, n_valid);
+  const uint32_t* ck = p.cand_key + (size_t)r * p.C;
+  const int32_t* ci = p.cand_idx + (size_t)r * p.C;
+  BucketEntries ent;
+  bucket_load(ent, ck, ci, 0, kBucketEarly, min(p.C, kMaxC));
+  const int cnt = min(p.cand_cnt[(size_t)r * p.cnt_stride], p.C);  // >= k_eff by construction
+  const int take = min(k_eff, cnt);
+  if (cnt >= 1) {
+    bucket_load(ent, ck, ci, kBucketEarly, kBucketPer, cnt);
+    if (bucket_rank_topk<kBits, 4>(p, r, ent, cnt, take, (uint64_t*)lds, (uint32_t*)(lds + kMaxC * 8), scratch))
+      return;
+  }
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
+  __syncthreads();
+  uint32_t theta = 0u;
+  int need = 1 << 30;
+  if (cnt > take) block_kth_key(skey, cnt, take, hist, &theta, &need);
+  // winners in list order, i.e. index order; padding (key 0) sorts last
+  block_ordered_emit(skey, ci, cnt, theta, need, scratch, [&](int pos, uint32_t u, int32_t ix) {
+    wkey[pos] = u;
+    widx[pos] = ix;
+  });
+  for (int i = take + (int)threadIdx.x; i < kSortN; i += blockDim.x) {
+    wkey[i] = 0u;
+    widx[i] = -1;
+  }
+  __syncthreads();
+  // stable by key: equal keys stay in index order, the tie rule
+  block_radix_sort_desc(wkey, widx, skey, (int32_t*)(skey + kSortN), skey + 2 * kSortN, scratch);
+  write_sorted(p, r, wkey, widx, take);
 }
 
 // Decode requests: the candidate list is unordered (<= C entries, a superset
@@ -439,8 +464,9 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
   static_assert(kMaxC >= 2 * kSortN + 256 * kSortWaves, "sort scratch must fit in skey");
   // one LDS buffer: the bucket path's order words and bucket counts, or the
   // sort path's candidate keys (skey) and winners (wkey, widx)
-  static_assert(kMaxC * 4 + 2 * kSortN * 4 <= kBucketLdsBytes, "sort path fits the buffer");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kBucketLdsBytes];
+  constexpr int kBits = 12;  // few workgroups: the finest buckets that fit
+  static_assert(kMaxC * 4 + 2 * kSortN * 4 <= bucket_lds_bytes(kBits), "sort path fits the buffer");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[bucket_lds_bytes(kBits)];
   uint32_t* const skey = (uint32_t*)lds;
   uint32_t* const wkey = skey + kMaxC;
   int32_t* const widx = (int32_t*)(wkey + kSortN);
@@ -462,7 +488,8 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
     take = min(k_eff, cnt);  // cnt >= k_eff by construction
     if (cnt >= 1) {
       bucket_load(ent, ck, ci, kBucketEarly, kBucketPer, cnt);  // the rest (zeros past the end)
-      if (bucket_rank_topk(p, r, ent, cnt, take, (uint64_t*)lds, (uint32_t*)(lds + kMaxC * 8), scratch)) return;
+      if (bucket_rank_topk<kBits, 8>(p, r, ent, cnt, take, (uint64_t*)lds, (uint32_t*)(lds + kMaxC * 8), scratch))
+        return;
     }
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
     if (threadIdx.x == 0) sh_n = 0;
