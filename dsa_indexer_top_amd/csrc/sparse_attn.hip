@@ -30,6 +30,9 @@
 // of a workgroup of 8 waves are merged in LDS first, so a row has at most 8
 // partials, or none when one workgroup covers it. A second kernel merges a
 // row's partials by the log-sum-exp rule.
+// A wave with more than one chunk gathers the next chunk's K rows while it
+// computes the current one (its V rows are requested at its start, ahead of
+// its S product); a wave with one chunk gathers K and V together.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -62,8 +65,8 @@ __device__ __forceinline__ int prow(int j) { return (j & 3) * 4 + (j >> 2); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, int MODE, int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void sparse_attn_kernel(AttnParams p) {
+template <int D, int MODE, int WAVES, bool PIPE>
+__device__ __forceinline__ void sparse_attn_body(const AttnParams& p) {
   using S = AttnShape<D>;
   static_assert((S::PSTRIDE / 4) % 64 == 16, "lane groups of a read must not share banks");
   __shared__ __attribute__((aligned(16))) unsigned char lds_v[WAVES][16 * S::PSTRIDE];
@@ -115,42 +118,59 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attn_kernel(AttnParams p
   for (int db = 0; db < S::DB; ++db) o[db] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   float m = -__builtin_inff(), l = 0.0f;
 
-  int raw_next = (e0 + (lane & 31) < e1) ? irow[e0 + (lane & 31)] : -1;
-  for (int c0 = e0; c0 < e1; c0 += kAttnChunk) {
-    const int raw = raw_next;
-    {
-      const int e = c0 + kAttnChunk + (lane & 31);
-      raw_next = e < e1 ? irow[e] : -1;
-    }
+  struct Chunk {
+    bf16x8 kf[2][S::KS];
+    i32x4 vv[S::VL];  // !PIPE: gathered with K
+    uint32_t vmask;
+    int key;
+  };
+  // index entries of the chunk at c (lanes l and l + 32: entry c + l % 32)
+  auto load_idx = [&](int c) -> int {
+    const int e = c + (lane & 31);
+    return e < e1 ? irow[e] : -1;
+  };
+  // a chunk's gathers: K rows as A fragments, V rows into registers
+  auto gather = [&](Chunk& ch, int raw) {
     const bool valid = raw >= 0 && raw <= pos && raw < p.n_k;
     // K/V row of this entry: the token itself, or its pool row under paging
     // (an invalid entry reads row 0 of the request, or of the pool; its weight is 0)
     const int key = !valid ? 0 : (paged ? (int)paged_row(p.kv, b, raw) : raw);
-    const uint32_t vmask = (uint32_t)ballot(valid);  // bit j: entry c0 + j is valid
-
-    // gathers: K rows as A fragments, V rows into registers
-    bf16x8 kf[2][S::KS];
+    ch.vmask = (uint32_t)ballot(valid);  // bit j: entry j of the chunk is valid
+    ch.key = key;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int kj = __shfl(key, 16 * nb + i16, 64);
       const unsigned char* krow = kb + (size_t)kj * (D * 2) + g * (D / 2);
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) kf[nb][ks] = *(const bf16x8*)(krow + 16 * ks);
+      for (int ks = 0; ks < S::KS; ++ks) ch.kf[nb][ks] = *(const bf16x8*)(krow + 16 * ks);
     }
+    if constexpr (!PIPE) {
+#pragma unroll
+      for (int i = 0; i < S::VL; ++i) {
+        const int vj = __shfl(key, S::RPI * i + vr, 64);
+        ch.vv[i] = *(const i32x4*)(vb + (size_t)vj * (D * 2) + 16 * vc);
+      }
+    }
+  };
+  auto compute = [&](const Chunk& ch) {
+    const uint32_t vmask = ch.vmask;
     i32x4 vv[S::VL];
 #pragma unroll
     for (int i = 0; i < S::VL; ++i) {
-      const int vj = __shfl(key, S::RPI * i + vr, 64);
-      vv[i] = *(const i32x4*)(vb + (size_t)vj * (D * 2) + 16 * vc);
+      if constexpr (PIPE) {
+        const int vj = __shfl(ch.key, S::RPI * i + vr, 64);
+        vv[i] = *(const i32x4*)(vb + (size_t)vj * (D * 2) + 16 * vc);
+      } else {
+        vv[i] = ch.vv[i];
+      }
     }
-
     // S^T = K . Q^T: lane holds head i16, keys 16*nb + 4*g + r
     f32x4 s[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       s[nb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[nb][ks], qb[ks], s[nb], 0, 0, 0);
+      for (int ks = 0; ks < S::KS; ++ks) s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.kf[nb][ks], qb[ks], s[nb], 0, 0, 0);
     }
 
     // stage V as pair rows: load i holds keys RPI*i + vr, load i + VL/2 the
@@ -216,6 +236,36 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attn_kernel(AttnParams p
 #pragma unroll
       for (int w = 0; w < 4; ++w) a[w] = *(const int*)(vl + prow(4 * g + w) * S::PSTRIDE + 4 * (16 * db + i16));
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[db], 0, 0, 0);
+    }
+  };
+
+  if constexpr (PIPE) {
+    // the next chunk's K rows are gathered while this chunk is computed (its
+    // V rows are requested at its start, ahead of its S product); each index
+    // load is issued before the gathers it does not feed
+    Chunk ca, cb;
+    int ra = load_idx(e0);
+    int rb = load_idx(e0 + kAttnChunk);
+    if (e0 < e1) gather(ca, ra);
+    for (int c0 = e0; c0 < e1; c0 += 2 * kAttnChunk) {
+      ra = load_idx(c0 + 2 * kAttnChunk);
+      const bool has_b = c0 + kAttnChunk < e1;
+      if (has_b) gather(cb, rb);
+      compute(ca);
+      if (!has_b) break;
+      rb = load_idx(c0 + 3 * kAttnChunk);
+      if (c0 + 2 * kAttnChunk < e1) gather(ca, ra);
+      compute(cb);
+    }
+  } else {
+    // one chunk at a time, K and V gathered together (waves with one chunk)
+    Chunk ca;
+    int raw_next = load_idx(e0);
+    for (int c0 = e0; c0 < e1; c0 += kAttnChunk) {
+      const int raw = raw_next;
+      raw_next = load_idx(c0 + kAttnChunk);
+      gather(ca, raw);
+      compute(ca);
     }
   }
   // the four lane groups summed different keys of the same head
@@ -303,6 +353,20 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attn_kernel(AttnParams p
   }
 }
 
+// Waves with one chunk keep the compiler's occupancy choice. With the next
+// chunk's K fragments in flight, the D = 128 kernels need more than 128
+// registers (VGPRs and AGPRs together), so they are held to two waves per SIMD
+// (256), which they fit without spilling.
+template <int D, int MODE, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void sparse_attn_kernel(AttnParams p) {
+  sparse_attn_body<D, MODE, WAVES, false>(p);
+}
+template <int D, int MODE, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_pipe_kernel(
+    AttnParams p) {
+  sparse_attn_body<D, MODE, WAVES, true>(p);
+}
+
 // Merges the partials of one (query, head) per wave:
 // M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s o_s 2^(m_s - M) / L
 // (m in log2 units; a partial with no valid entry has m = -inf, l = 0, o = 0).
@@ -350,20 +414,41 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     p.lse[(size_t)row * p.H + h] = L > 0.0f ? (M + __log2f(L)) * 0.6931471805599453f : -__builtin_inff();
 }
 
+template <int D, bool PIPE>
+static void launch_attn_form(const AttnParams& p, hipStream_t s) {
+  const int rows = p.B * p.n_q;
+  const int ns = p.nsplit;
+  const dim3 grid((unsigned)(((long)rows * ns + kAttnWaves - 1) / kAttnWaves));
+  const dim3 ggrid((unsigned)(rows * (ns / kAttnGroupWaves)));
+  if constexpr (PIPE) {
+    if (ns >= kAttnGroupWaves)
+      hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, kAttnGroup, kAttnGroupWaves>), ggrid, dim3(kAttnGroupWaves * kWave),
+                         0, s, p);
+    else if (ns > 1)
+      hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, kAttnSplit, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
+    else
+      hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, kAttnDirect, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
+  } else {
+    if (ns >= kAttnGroupWaves)
+      hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnGroup, kAttnGroupWaves>), ggrid, dim3(kAttnGroupWaves * kWave), 0, s,
+                         p);
+    else if (ns > 1)
+      hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnSplit, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
+    else
+      hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnDirect, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
+  }
+}
+
 template <int D>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s) {
   const int rows = p.B * p.n_q;
   const int ns = p.nsplit;
   if (ns < 1 || ns > 64 || (ns >= kAttnGroupWaves && ns % kAttnGroupWaves) || attn_nparts(ns) > kAttnMaxParts)
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(((long)rows * ns + kAttnWaves - 1) / kAttnWaves));
-  if (ns >= kAttnGroupWaves)
-    hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnGroup, kAttnGroupWaves>), dim3(rows * (ns / kAttnGroupWaves)),
-                       dim3(kAttnGroupWaves * kWave), 0, s, p);
-  else if (ns > 1)
-    hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnSplit, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
-  else
-    hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnDirect, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
+  // chunks per wave (the kernel's split of the list): prefetch only with more than one
+  const int per = ((p.topk + ns - 1) / ns + kAttnChunk - 1) / kAttnChunk;
+  if (per > 1) launch_attn_form<D, true>(p, s);
+  else launch_attn_form<D, false>(p, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || attn_nparts(ns) <= 1) return e;
   hipLaunchKernelGGL((attn_combine_kernel<D, kAttnMaxParts>), dim3((p.H + 3) / 4, rows), dim3(256), 0, s, p);
