@@ -221,6 +221,32 @@ def decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, config=4):
     return res
 
 
+def decode_gather_bench(dsa, torch, B, T, topk, steps, warmup, config=4):
+    """Decode attention alone at a batch large enough to load the HBM: B
+    requests over T-token caches (K and V: B * T * 512 bytes), k uniform random
+    indices per request (on the synthetic scores the indexer's picks are
+    spread the same way)."""
+    from dsa_inputs import make_attn_inputs
+    a = make_attn_inputs(B, 1, T, 16, 128, config=config, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(1_000_000 * config + 13)
+    idx = torch.randint(0, T, (B, 1, topk), generator=g, device="cuda", dtype=torch.int32)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms = []
+    for i in range(warmup + steps):
+        dsa.sparse_attn(a.q, a.k, a.v, idx, phase_events=ev)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            ms.append(ev[0].elapsed_time(ev[1]))
+    a_ms = sum(ms) / len(ms)
+    att_bytes = B * topk * 2 * 128 * 2  # gathered K and V rows
+    res = {"B": B, "context": T, "topk": topk, "attn_ms": a_ms, "attn_gather_GBps": att_bytes / a_ms / 1e6,
+           "attn_gather_hbm_frac": att_bytes / a_ms / 1e6 / PEAK_HBM_GBS}
+    log(f"decode attention B={B}: {a_ms * 1e3:.1f} us ({res['attn_gather_GBps']:.0f} GB/s of gathered rows)")
+    del a, idx
+    torch.cuda.empty_cache()
+    return res
+
+
 def paged_decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, page_size=64, config=6):
     """One decode token of B requests with seeded ragged context lengths
     (uniform in [2048, T]) over paged pools (page_size tokens, pages handed out
@@ -401,8 +427,9 @@ def main():
         print(json.dumps(stack200k(dsa, torch, L, topk, args)), flush=True)
         return
     if args.only == "decode":
-        print(json.dumps({f"decode_B{B}": decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
-                          for B in (1, 32)}), flush=True)
+        res = {f"decode_B{B}": decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2) for B in (1, 32)}
+        res["decode_attn_B256"] = decode_gather_bench(dsa, torch, 256, 200000, topk, max(3, args.steps), 2)
+        print(json.dumps(res), flush=True)
         return
     if args.only == "overlap":
         print(json.dumps(overlap_bench(dsa, torch, max(2, args.steps))), flush=True)
@@ -481,6 +508,7 @@ def main():
         for B in (1, 32):
             log(f"decode B={B}")
             extra[f"decode_B{B}"] = decode_bench(dsa, torch, B, 200000, 47, topk, args.steps, 2)
+        extra["decode_attn_B256"] = decode_gather_bench(dsa, torch, 256, 200000, topk, max(3, args.steps), 2)
         log("paged ragged decode B=32")
         extra["decode_paged_ragged_B32"] = paged_decode_bench(dsa, torch, 32, 200000, 47, topk, args.steps, 2)
         extra["topk_overlap_47_layers"] = overlap_bench(dsa, torch, max(2, args.steps))
