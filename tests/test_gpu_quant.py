@@ -78,3 +78,26 @@ def test_quant_long_rows(dsa):
     g = torch.Generator(device="cuda").manual_seed(1_000_000 * 12 + 3)
     x = torch.randn(37, 16400, generator=g, device="cuda") * torch.logspace(-3, 3, 37, device="cuda")[:, None]
     check(dsa, x.to(torch.bfloat16))
+
+
+def test_quant_every_bf16_value(dsa):
+    """Every finite bf16 pattern in rows whose maxima sweep 60 binades (2^-30 ..
+    2^29, mantissas varied), and rows with the smallest scales (where the
+    kernel divides exactly): codes and scales bit for bit."""
+    say("quant every bf16 value")
+    pats = np.arange(65536, dtype=np.uint32)
+    x_all = (pats << 16).view(np.float32)
+    x_all = x_all[np.isfinite(x_all)]
+    rng = np.random.default_rng(1_000_000 * 11 + 7)
+    amaxes = [np.float32(2.0 ** e * (1 + rng.integers(0, 128) / 128)) for e in range(-30, 30)]
+    amaxes += [np.float32(2.0 ** -120), np.float32(1.5 * 2.0 ** -126), np.float32(2.0 ** -130)]
+    rows = []
+    for a in amaxes:
+        a = np.float32(torch.tensor(float(a)).to(torch.bfloat16).float().item())  # a bf16 value
+        v = x_all[np.abs(x_all) <= a]
+        row = np.zeros(65536, dtype=np.float32)
+        row[:v.size] = v
+        row[-1] = a          # the row's maximum is a
+        rows.append(row)
+    x = torch.from_numpy(np.stack(rows)).to(torch.bfloat16).cuda()
+    check(dsa, x)
