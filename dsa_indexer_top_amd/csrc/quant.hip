@@ -18,7 +18,7 @@
 // underflows it can differ from fl32(x / s) in the last bits, but such
 // quotients (below 2^-126) are far below half the smallest e4m3fn magnitude
 // (2^-10), so the code is a signed zero either way; the sign is restored from
-// x, since a -0 input would otherwise come out +0. An exhaustive check of
+// x, since a -0 input would otherwise come out +0. A standalone exhaustive check of
 // every bf16 x against every bf16 row maximum amax with s >= 2^-100 (1.04e9
 // pairs, |x| <= amax) gave identical codes. Rows with a smaller scale (where
 // y would overflow) divide exactly.
