@@ -14,14 +14,15 @@
 // Muller et al., Handbook of Floating-Point Arithmetic, the FMA-based
 // division chapter): q = fl32(x y), e = fma(-q, s, x) (exact), q' = fma(e, y, q)
 // is the correctly rounded x / s when nothing underflows. Three operations
-// per value instead of the ~10 of a full IEEE division. Where the quotient
-// underflows it can differ from fl32(x / s) in the last bits, but such
-// quotients (below 2^-126) are far below half the smallest e4m3fn magnitude
-// (2^-10), so the code is a signed zero either way; the sign is restored from
-// x, since a -0 input would otherwise come out +0. A standalone exhaustive check of
-// every bf16 x against every bf16 row maximum amax with s >= 2^-100 (1.04e9
-// pairs, |x| <= amax) gave identical codes. Rows with a smaller scale (where
-// y would overflow) divide exactly.
+// per value instead of the ~10 of a full IEEE division. Where the residual e
+// underflows (tiny x and s), q' can differ from fl32(x / s) in its low bits;
+// with s >= 2^-100 that happens only for quotients below 2^-13, under half
+// the smallest e4m3fn magnitude (2^-10), so the code is a signed zero either
+// way. The sign is restored from x, since a -0 input would otherwise come out
+// +0. A standalone exhaustive check of every bf16 x against every bf16 row
+// maximum amax with s >= 2^-100 (1.04e9 pairs, |x| <= amax) gave identical
+// codes (largest deviating quotient 1.2e-4). Rows with a smaller scale
+// divide exactly.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
