@@ -352,22 +352,17 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
   __syncthreads();
   int32_t* oi = p.out_idx + (size_t)r * p.topk;
   float* os = p.out_scores ? p.out_scores + (size_t)r * p.topk : nullptr;
+  // One group of H entries per thread at a time: each steps through its
+  // bucket with no branch between the LDS reads, so that they are in flight
+  // together (a step past the bucket re-reads its last member and is not
+  // counted). A list of at most H entries per thread is ranked from the
+  // entries in registers (entries past the prefix skipped); a longer one by
   // positions j < prefix of the bucket-ordered words, consecutive positions on
-  // consecutive lanes (so a wave's lanes mostly share a bucket), H per thread
-  // at a time: each steps through its bucket with no branch between the LDS
-  // reads, so that they are in flight together (a step past the bucket
-  // re-reads its last member and is not counted)
-  for (int g0 = 0; g0 * kFinNTDecode < prefix; g0 += H) {
-    uint64_t mine[H];
-    int s0[H], rank[H], last[H], len[H], wrun = 0;
+  // consecutive lanes (so a wave's lanes mostly share a bucket).
+  auto rank_group = [&](const uint64_t (&mine)[H], const int (&s0)[H], const int (&len)[H]) {
+    int rank[H], last[H], wrun = 0;
 #pragma unroll
     for (int q = 0; q < H; ++q) {
-      const int j = threadIdx.x + (g0 + q) * kFinNTDecode;
-      const bool in = j < prefix;
-      mine[q] = word[in ? j : 0];
-      const uint32_t bk = (umax - (uint32_t)(mine[q] >> 32)) >> shift;
-      s0[q] = (int)base[in ? bk : 0u];
-      len[q] = in ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : cnt) - s0[q] : 0;
       rank[q] = s0[q];
       last[q] = s0[q] + max(len[q] - 1, 0);
       wrun = max(wrun, len[q]);
@@ -384,10 +379,38 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
     }
 #pragma unroll
     for (int q = 0; q < H; ++q) {
-      if (len[q] > 0 && rank[q] < take) {  // len > 0: a position below the prefix
+      if (len[q] > 0 && rank[q] < take) {  // len > 0: an entry of the prefix
         oi[rank[q]] = (int32_t)~(uint32_t)mine[q];
         if (os) os[rank[q]] = key_score((uint32_t)(mine[q] >> 32));
       }
+    }
+  };
+  if (cnt <= H * kFinNTDecode) {
+    uint64_t mine[H];
+    int s0[H], len[H];
+#pragma unroll
+    for (int q = 0; q < H; ++q) {
+      const bool in = threadIdx.x + q * kFinNTDecode < cnt;
+      const uint32_t bk = in ? (umax - v.u[q]) >> shift : 0u;
+      s0[q] = (int)base[bk];
+      len[q] = in && s0[q] < prefix ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : cnt) - s0[q] : 0;
+      mine[q] = ((uint64_t)v.u[q] << 32) | (uint32_t)~(uint32_t)v.x[q];
+    }
+    rank_group(mine, s0, len);
+  } else {
+    for (int g0 = 0; g0 * kFinNTDecode < prefix; g0 += H) {
+      uint64_t mine[H];
+      int s0[H], len[H];
+#pragma unroll
+      for (int q = 0; q < H; ++q) {
+        const int j = threadIdx.x + (g0 + q) * kFinNTDecode;
+        const bool in = j < prefix;
+        mine[q] = word[in ? j : 0];
+        const uint32_t bk = (umax - (uint32_t)(mine[q] >> 32)) >> shift;
+        s0[q] = (int)base[in ? bk : 0u];
+        len[q] = in ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : cnt) - s0[q] : 0;
+      }
+      rank_group(mine, s0, len);
     }
   }
   for (int i = take + (int)threadIdx.x; i < p.topk; i += blockDim.x) {
