@@ -195,6 +195,13 @@ dsa_status run_attn(const dsa::AttnParams& p, hipStream_t s) {
 
 namespace dsa {
 
+// Byte offset of the decode plan (followed by the histograms) in the indexer
+// workspace of a decode call (n_q == 1): after the candidate lists and keys.
+size_t indexer_decode_plan_offset(int B, int n_k, int topk) {
+  const size_t C = (size_t)cand_capacity(topk, true);
+  return 2 * round_up((size_t)B * C * 4, 256) + (size_t)B * decode_key_stride(n_k) * 4;
+}
+
 size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk) {
   const size_t rows = (size_t)B * n_q;
   const size_t C = (size_t)cand_capacity(topk, n_q == 1);
@@ -420,6 +427,15 @@ static dsa_status stack_run(const dsa_stack_args* a, const dsa::PagedKV* kv, con
   st = check_workspace(a->workspace, a->workspace_bytes, stack_ws(a), what);
   if (st != DSA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  // decode: after the first F layer the histograms and counters are zero and
+  // the ragged plan is built, unless the attention partials (at the start of
+  // the shared workspace) reach the plan
+  const bool decode = a->indexer.n_q == 1;
+  const bool keep_prepared =
+      decode && dsa::attn_workspace_bytes(a->attn.B, a->attn.n_q, a->attn.n_k, a->attn.n_heads, a->attn.head_dim,
+                                          a->attn.topk) <= dsa::indexer_decode_plan_offset(a->indexer.B, a->indexer.n_k,
+                                                                                          a->indexer.topk);
+  bool prepared = false;
   for (int l = 0; l < n; ++l) {
     if (a->layer_events) {
       const hipError_t e = hipEventRecord((hipEvent_t)a->layer_events[l], s);
@@ -431,8 +447,10 @@ static dsa_status stack_run(const dsa_stack_args* a, const dsa::PagedKV* kv, con
                                                   fp8 ? a->q_scale[l] : nullptr, fp8 ? a->k_scale[l] : nullptr,
                                                   a->idx_buf, nullptr, nullptr, a->workspace);
       if (kv) ip.kv = *kv;
+      ip.skip_prepare = prepared ? 1 : 0;
       st = run_indexer(ip, s);
       if (st != DSA_OK) return st;
+      prepared = keep_prepared;
     }
     // every layer: sparse attention over the cached indices
     dsa::AttnParams ap = make_attn_params(&a->attn, a->q[l], a->k[l], a->v[l], a->idx_buf, a->out[l],

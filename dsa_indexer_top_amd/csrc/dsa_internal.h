@@ -86,6 +86,8 @@ struct IndexerParams {
                         // block, planned on the device when lengths are ragged (kv.seq_lens)
   PagedKV kv;           // decode only: paged pools (kv.block_table) or flat
   void* const* ev;      // optional phase events (3): before scores, after scores, after select
+  int skip_prepare;     // decode: histograms and counters already zero and the ragged
+                        // plan already built for this kv (a later F layer of a stack)
 };
 
 // Records phase event i (if any) on the stream.
@@ -115,6 +117,7 @@ constexpr int kAttnPartStride = D + 4;
 inline int attn_part_stride(int D) { return D + 4; }
 
 size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk);
+size_t indexer_decode_plan_offset(int B, int n_k, int topk);
 size_t attn_workspace_bytes(int B, int n_q, int n_k, int H, int D, int topk);
 int attn_nsplit(int B, int n_q, int topk);
 // Waves per workgroup that merge their splits in LDS, and the partials per

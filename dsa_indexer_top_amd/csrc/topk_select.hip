@@ -213,6 +213,7 @@ struct FinalizeParams {
   const int32_t* cand_idx;
   const int32_t* cand_cnt;  // row r at cand_cnt[r * cnt_stride]
   int cnt_stride;
+  uint32_t* dec_hist;  // decode: histogram rows, zeroed (with the counter) once read
   const uint32_t* full_keys;  // decode: [rows, decode_key_stride(n_k)] keys for the overflow path
   PagedKV kv;                 // decode: per-request lengths (kv.seq_lens) or none
   int32_t* out_idx;
@@ -504,7 +505,16 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
   // the list's first entries are loaded together with its count
   BucketEntries ent;
   bucket_load(ent, ck, ci, 0, kBucketEarly, min(p.C, kMaxC));
-  const int cnt = p.cand_cnt[(size_t)r * p.cnt_stride];
+  // the request's histogram row and counter are left zero for the next
+  // decode call on this workspace: the bins are no longer read, the counter
+  // once every thread has it
+  __shared__ int sh_cnt;
+  if (threadIdx.x == 0) sh_cnt = p.cand_cnt[(size_t)r * p.cnt_stride];
+  uint32_t* gh = p.dec_hist + (size_t)r * kDecodeHistStride;
+  for (int i = threadIdx.x; i < kDecodeCntOffset; i += blockDim.x) gh[i] = 0u;
+  __syncthreads();
+  const int cnt = sh_cnt;
+  if (threadIdx.x == 0) gh[kDecodeCntOffset] = 0u;
   int take;
   bool ordered;  // winners already in index order
   if (cnt <= p.C) {
@@ -614,6 +624,7 @@ hipError_t launch_topk_finalize(const IndexerParams& ip, int rows, hipStream_t s
   p.cand_idx = ip.cand_idx;
   p.cand_cnt = ip.cand_cnt;
   p.cnt_stride = ip.cnt_stride;
+  p.dec_hist = ip.dec_hist;
   p.full_keys = ip.dec_keys;
   p.kv = ip.kv;
   p.out_idx = ip.out_idx;
@@ -979,10 +990,13 @@ static void launch_decode_scores_t(const IndexerParams& p, hipStream_t s) {
 
 hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
   // zero the histograms and counters (a kernel, not a memset node), and plan
-  // ragged score blocks
-  const size_t nz = (size_t)p.B * kDecodeHistStride;
-  hipLaunchKernelGGL(decode_prepare_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 1024)), dim3(256), 0,
-                     s, p, nz, p.B + kDecodeTargetBlocks);
+  // ragged score blocks; a later F layer of a stack finds them zero (the
+  // finalize kernel clears its request's row) and the plan built
+  if (!p.skip_prepare) {
+    const size_t nz = (size_t)p.B * kDecodeHistStride;
+    hipLaunchKernelGGL(decode_prepare_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 1024)), dim3(256), 0,
+                       s, p, nz, p.B + kDecodeTargetBlocks);
+  }
   hipError_t e = record_phase(p.ev, 0, s);
   if (e != hipSuccess) return e;
   const bool two = p.H > 32;
