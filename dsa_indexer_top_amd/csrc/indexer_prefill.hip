@@ -399,6 +399,9 @@ void indexer_prefill_kernel(IndexerParams p) {
   // have negative bit patterns; then the head weights and the head sum). Each
   // k-step chunk is fenced with sched_barrier so that one wave keeps both the
   // matrix core and the VALU busy; B fragments are read two k-steps ahead.
+  // With two k-steps per half (fp8), a half can take its B fragments from
+  // `pre` (PIN) and read the next half's (tile nkt, block nnb) into it after
+  // its first MFMAs (POUT); halves separated by the tile barrier do not.
   // Returns this lane's partial score of key (lane & 31) of the previous half
   // over its 16 * MB heads (0 when EPI is false).
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type BFrag;
@@ -417,13 +420,23 @@ void indexer_prefill_kernel(IndexerParams p) {
   };
 
   constexpr int SIDE_KS = KS > 1 ? 1 : 0;  // chunk that also carries the previous tile's filter
-  auto half_step = [&](auto EPI_T, auto MMA_T, const unsigned char* kt, int nb, f32x16 (&acc)[MB],
-                       const f32x16 (&prev)[MB], auto&& side) -> float {
+  // fp8 (two k-steps per half): the next half's B fragments are read during
+  // this half (after its first MFMAs), so its MFMAs need not wait for LDS
+  constexpr bool kPre = FP8 && KS == 2;
+  BFrag pre[2];
+  auto half_step = [&](auto EPI_T, auto MMA_T, auto PIN_T, auto POUT_T, const unsigned char* kt, int nb,
+                       const unsigned char* nkt, int nnb, f32x16 (&acc)[MB], const f32x16 (&prev)[MB],
+                       auto&& side) -> float {
     constexpr bool EPI = decltype(EPI_T)::value;
     constexpr bool MMA = decltype(MMA_T)::value;
+    constexpr bool PIN = decltype(PIN_T)::value && kPre && MMA;
+    constexpr bool POUT = decltype(POUT_T)::value && kPre && MMA;
     const int brow = 32 * nb + i32;
     BFrag bf[3];
-    if constexpr (MMA) {
+    if constexpr (PIN) {
+      bf[0] = pre[0];
+      bf[1] = pre[1];
+    } else if constexpr (MMA) {
       bf[0] = read_b(kt, brow, 0);
       if (KS > 1) bf[1 % 3] = read_b(kt, brow, KS > 1 ? 1 : 0);
     }
@@ -440,6 +453,12 @@ void indexer_prefill_kernel(IndexerParams p) {
           else
             acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], bf[ks % 3],
                                                                ks == 0 ? f32x16{} : acc[mb], 0, 0, 0);
+        }
+        if constexpr (POUT) {
+          if (ks == 0) {
+            pre[0] = read_b(nkt, 32 * nnb + i32, 0);
+            pre[1] = read_b(nkt, 32 * nnb + i32, 1);
+          }
         }
       }
       if constexpr (EPI) {
@@ -541,7 +560,7 @@ void indexer_prefill_kernel(IndexerParams p) {
   // then the only outstanding loads the MFMAs could be made to wait for.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (kend > 0) half_step(FalseT{}, TrueT{}, lds_k[0], 0, accA, accB, no_side);
+  if (kend > 0) half_step(FalseT{}, TrueT{}, FalseT{}, TrueT{}, lds_k[0], 0, lds_k[0], 1, accA, accB, no_side);
   // One iteration, tile = 128 keys in four 32-key quarters q0..q3 (q0 was
   // multiplied in the previous iteration): q1 (+ epilogue of q0, + the filter
   // of the previous tile's keys 64..127, committed right after), q2 (+ epilogue
@@ -568,17 +587,19 @@ void indexer_prefill_kernel(IndexerParams p) {
     // waves could read different values and enter different barriers.
     const int par = tile % 3, prev = (tile + 2) % 3;
     float q0 = 0.0f, q1 = 0.0f, q2 = 0.0f, q3 = 0.0f;
-    if (mine) q0 = half_step(TrueT{}, TrueT{}, lds_k[cur], 1, accB, accA, filter_compute);
+    if (mine)
+      q0 = half_step(TrueT{}, TrueT{}, TrueT{}, TrueT{}, lds_k[cur], 1, lds_k[cur], 2, accB, accA, filter_compute);
     else filter_compute();
     filter_commit(par);  // the previous tile's keys 64..127
     if (mine) {
-      q1 = half_step(TrueT{}, TrueT{}, lds_k[cur], 2, accA, accB, no_side);
+      q1 = half_step(TrueT{}, TrueT{}, TrueT{}, TrueT{}, lds_k[cur], 2, lds_k[cur], 3, accA, accB, no_side);
       pend_p0 = q0;
       pend_p1 = q1;
       pend_ksc = ksc0;
       pend_base = base;
       pend_end = kend;
-      q2 = half_step(TrueT{}, TrueT{}, lds_k[cur], 3, accB, accA, filter_compute);
+      q2 = half_step(TrueT{}, TrueT{}, TrueT{}, FalseT{}, lds_k[cur], 3, lds_k[cur], 0, accB, accA,
+                     filter_compute);
     } else {
       filter_compute();
     }
@@ -594,9 +615,11 @@ void indexer_prefill_kernel(IndexerParams p) {
     if (tile + 2 < n_tiles) dma_tile(tile + 2, cur);
     if (mine) {
       if (mine_next)
-        q3 = half_step(TrueT{}, TrueT{}, lds_k[cur ^ 1], 0, accA, accB, read_flags);
+        q3 = half_step(TrueT{}, TrueT{}, FalseT{}, TrueT{}, lds_k[cur ^ 1], 0, lds_k[cur ^ 1], 1, accA, accB,
+                       read_flags);
       else
-        q3 = half_step(TrueT{}, FalseT{}, lds_k[cur], 0, accA, accB, read_flags);
+        q3 = half_step(TrueT{}, FalseT{}, FalseT{}, FalseT{}, lds_k[cur], 0, lds_k[cur], 0, accA, accB,
+                       read_flags);
       pend_p0 = q2;
       pend_p1 = q3;
       pend_ksc = ksc1;
