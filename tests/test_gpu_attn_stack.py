@@ -84,10 +84,13 @@ def test_attn_decode_split(dsa, B, n_k, topk):
     (1, 128, 3000, 12, 64, 700),      # 16 splits: two workgroup partials, ragged last chunk
     (4, 16, 5000, 16, 128, 1500),     # 32 splits: four workgroup partials, empty last splits
     (1, 1, 5000, 5, 64, 2048),        # 64 splits, D = 64, 5 heads
+    (1, 1024, 3000, 16, 64, 1024),    # 2 splits of 16 chunks each (K of the next chunk read ahead), D = 64
+    (1, 2048, 4096, 8, 128, 512),     # one wave per row, 16 chunks (read ahead), D = 128
 ])
 def test_attn_split_forms(dsa, B, n_q, n_k, H, D, topk):
     """Each launch form of the split-K rule (about 2048 waves per call): direct,
-    per-wave partials, and 8-wave workgroups merging in LDS with 1..8 partials."""
+    per-wave partials, and 8-wave workgroups merging in LDS with 1..8 partials;
+    with one chunk per wave and with several (the next chunk's K read ahead)."""
     say(f"attn forms B={B} n_q={n_q} n_k={n_k} H={H} D={D} k={topk}")
     a = make_attn_inputs(B, n_q, n_k, H, D, config=34)
     _check_attn(dsa, a, _random_idx(B, n_q, n_k, topk, n_k - n_q, 3, junk=True))
