@@ -239,17 +239,20 @@ __device__ void write_sorted(const FinalizeParams& p, int r, const uint32_t* wke
 constexpr int kMaxC = 8192;
 constexpr int kMaxTopk = 2048;
 
-// Exact top-k of an unordered decode candidate list (1 <= cnt <= kMaxC
-// entries, distinct indices, a superset of the top-k) by ranking instead of
-// sorting. Entries go to 2^kBucketBits buckets by the top bits of (max key -
-// key), so that every entry of a lower bucket has a larger key; an LDS
-// counting pass returns each entry's slot in its bucket, an exclusive scan of
-// the counts gives each bucket's first rank, and each entry's 64-bit order
-// word (key, ~index) is stored at its slot. An entry's rank is its bucket's
-// first rank plus the members of its bucket with a larger order word (larger
-// key, or equal key and lower index); entries ranked below `take` are written
-// straight to their output slots. If a bucket holds more than kBucketMaxRun
-// entries (heavy ties), it returns false before writing any output.
+// Exact top-k of a candidate list (1 <= cnt <= kMaxC entries, distinct
+// indices, a superset of the top-k; any order: a prefill row's list is in
+// index order, a decode request's is not) by ranking instead of sorting.
+// Entries go to 2^kBucketBits buckets by the top bits of (max key - key), so
+// that every entry of a lower bucket has a larger key; an LDS counting pass
+// returns each entry's slot in its bucket, and an exclusive scan of the counts
+// gives each bucket's first rank. Buckets are in rank order, so only the
+// prefix up to the end of the bucket holding rank take - 1 can reach the top
+// k; those entries store their 64-bit order word (key, ~index) at their slot.
+// An entry's rank is its bucket's first rank plus the members of its bucket
+// with a larger order word (larger key, or equal key and lower index), and
+// entries ranked below `take` are written straight to their output slots. If
+// a bucket holds more than kBucketMaxRun entries (heavy ties), it returns
+// false before writing any output.
 static_assert(kFinNTPrefill == kFinNTDecode, "one bucket layout for both finalize kernels");
 constexpr int kBucketPer = kMaxC / kFinNTDecode;  // entries per thread
 constexpr int kBucketEarly = kBucketPer / 2;      // of them loaded before the count is known
