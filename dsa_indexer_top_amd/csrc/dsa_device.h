@@ -42,7 +42,7 @@ __device__ __forceinline__ int lane_id() {
   return l;
 }
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // Number of set bits of `m` below this lane.
 __device__ __forceinline__ int mbcnt(uint64_t m) {

@@ -509,9 +509,10 @@ void indexer_prefill_kernel(IndexerParams p) {
     if constexpr (DUMP) {
       if (valid) p.dump[row * (size_t)p.n_k + key] = canon_zero(f_score);
     }
-    const uint64_t am = ballot(valid && f_score > theta_f);
+    const bool take = valid && f_score > theta_f;
+    const uint64_t am = ballot(take);
     if (am) {
-      if ((am >> lane) & 1ull) {
+      if (take) {
         // 32-bit byte offset from the row's (scalar) list bases: no 64-bit address math
         const uint32_t off = 4u * (uint32_t)(cnt + mbcnt(am));
         *(uint32_t*)((unsigned char*)ckey + off) = score_key(f_score);
