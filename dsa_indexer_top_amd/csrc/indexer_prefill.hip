@@ -45,7 +45,8 @@ constexpr int kMaxPrefillWaves = 8;
 constexpr int kTileKeys = 64;                  // keys per LDS sub-tile and per filter commit
 constexpr int kIterKeys = 2 * kTileKeys;       // keys per loop iteration (one barrier)
 // Appends a list may receive between the commit that flags it as nearly full
-// and the shrink that serves the flag: the flagging commit and three more.
+// and the shrink that serves the flag: the flagging commit and the next one,
+// 128 keys each.
 constexpr int kListMargin = 4 * kTileKeys;
 
 template <int D, bool FP8>
@@ -479,17 +480,22 @@ void indexer_prefill_kernel(IndexerParams p) {
   };
   using TrueT = std::integral_constant<bool, true>;
   using FalseT = std::integral_constant<bool, false>;
-  // Streaming filter of one finished tile, split in two. filter_compute runs
-  // inside a chunk of the next half tile, so its dependency chain (join the
+  // Streaming filter, 64 keys (two half tiles) at a time. filter_compute runs
+  // inside a chunk of a later half tile, so its dependency chain (join the
   // two half-tile partials with v_permlane32_swap: lane l < 32 gets key l of
-  // half 0, lane l >= 32 key l of half 1; order key; compare; ballot) hides
-  // behind MFMAs. filter_commit (after that half tile) takes the rare branch:
-  // append the accepted keys and, when the list is nearly full, shrink it.
-  // A tile is pending from the end of its second half until the next commit;
-  // with nothing pending, pend_end = 0 makes every lane invalid.
+  // half 0, lane l >= 32 key l of half 1) hides behind MFMAs. filter_commit,
+  // once per iteration after the barrier, compares both pending groups of 64
+  // (the previous tile's keys 64..127, then this tile's 0..63) with the
+  // threshold, appends the accepted keys in key order and, when the list is
+  // nearly full, flags it for a shrink. With nothing pending, an end of 0
+  // makes every lane of that group invalid.
   float pend_p0 = 0.0f, pend_p1 = 0.0f, pend_ksc = 1.0f;
   int pend_base = 0, pend_end = 0;
   float f_score = 0.0f;
+  // the previous tile's keys 64..127, computed during the first quarter and
+  // committed with this tile's keys 0..63 after the barrier
+  float f_score_a = 0.0f;
+  int pend_a_base = 0, pend_a_end = 0;
   // theta as a float: the order key is strictly monotone on scores, so
   // key > theta  <=>  score > key_score(theta) (and -inf accepts all).
   float theta_f = -__builtin_inff();
@@ -501,26 +507,43 @@ void indexer_prefill_kernel(IndexerParams p) {
     f_score = score;
     asm volatile("" : "+v"(f_score));
   };
+  auto filter_compute_a = [&]() {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pend_p0), __float_as_uint(pend_p1),
+                                                     false, false);
+    float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if constexpr (FP8) score *= pend_ksc;
+    f_score_a = score;
+    asm volatile("" : "+v"(f_score_a));
+  };
   // par: the iteration mod 3; a full list raises flag bit `wave` of
   // flags[par], which the workgroup reads after the next barrier and serves.
   auto filter_commit = [&](int par) {
-    const int key = pend_base + lane;
-    const bool valid = key < pend_end;
+    const int key_a = pend_a_base + lane, key = pend_base + lane;
+    const bool valid_a = key_a < pend_a_end, valid = key < pend_end;
     if constexpr (DUMP) {
+      if (valid_a) p.dump[row * (size_t)p.n_k + key_a] = canon_zero(f_score_a);
       if (valid) p.dump[row * (size_t)p.n_k + key] = canon_zero(f_score);
     }
-    const bool take = valid && f_score > theta_f;
-    const uint64_t am = ballot(take);
-    if (am) {
+    const bool take_a = valid_a && f_score_a > theta_f, take = valid && f_score > theta_f;
+    const uint64_t am_a = ballot(take_a), am = ballot(take);
+    if (am_a | am) {
+      // list order = key order: the previous tile's keys first
+      // 32-bit byte offsets from the row's (scalar) list bases: no 64-bit address math
+      if (take_a) {
+        const uint32_t off = 4u * (uint32_t)(cnt + mbcnt(am_a));
+        *(uint32_t*)((unsigned char*)ckey + off) = score_key(f_score_a);
+        *(int32_t*)((unsigned char*)cidx + off) = key_a;
+      }
+      const int cnt_b = cnt + popc64(am_a);
       if (take) {
-        // 32-bit byte offset from the row's (scalar) list bases: no 64-bit address math
-        const uint32_t off = 4u * (uint32_t)(cnt + mbcnt(am));
+        const uint32_t off = 4u * (uint32_t)(cnt_b + mbcnt(am));
         *(uint32_t*)((unsigned char*)ckey + off) = score_key(f_score);
         *(int32_t*)((unsigned char*)cidx + off) = key;
       }
-      cnt += popc64(am);
+      cnt = cnt_b + popc64(am);
       if (cnt > p.C - kListMargin && lane == 0) atomicOr(&shl.flags[par], 1u << wave);
     }
+    pend_a_end = 0;
     pend_end = 0;
   };
   // Called by the whole workgroup with the flags word it read after the
@@ -564,11 +587,11 @@ void indexer_prefill_kernel(IndexerParams p) {
   if (kend > 0) half_step(FalseT{}, TrueT{}, FalseT{}, TrueT{}, lds_k[0], 0, lds_k[0], 1, accA, accB, no_side);
   // One iteration, tile = 128 keys in four 32-key quarters q0..q3 (q0 was
   // multiplied in the previous iteration): q1 (+ epilogue of q0, + the filter
-  // of the previous tile's keys 64..127, committed right after), q2 (+ epilogue
-  // of q1), q3 (+ epilogue of q2, + the filter of keys 0..63), the barrier that
-  // publishes tile+1, the commit of keys 0..63, the load of tile+2 into the
-  // buffer `tile` leaves, and q0 of tile+1 (+ epilogue of q3). Keys 64..127
-  // are then pending for the filter.
+  // of the previous tile's keys 64..127), q2 (+ epilogue of q1), q3
+  // (+ epilogue of q2, + the filter of keys 0..63), the barrier that
+  // publishes tile+1, the commit of both filtered groups, the load of tile+2
+  // into the buffer `tile` leaves, and q0 of tile+1 (+ epilogue of q3). Keys
+  // 64..127 are then pending for the filter.
   auto iteration = [&](int tile) {
     const int cur = tile & 1;
     const bool more = tile + 1 < n_tiles;
@@ -580,18 +603,16 @@ void indexer_prefill_kernel(IndexerParams p) {
       ksc0 = (mine && base + lane < kend) ? kscale[base + lane] : 0.0f;
       ksc1 = (mine && base + kTileKeys + lane < kend) ? kscale[base + kTileKeys + lane] : 0.0f;
     }
-    // Flag words rotate over three iterations: iteration t writes word t % 3
-    // (one commit before its barrier, one after), iteration t+1 reads it
-    // after its barrier and serves it. A wave may already be committing the
-    // keys of iteration t+2 (before barrier t+2) while a slower one still
-    // reads word t % 3, so t+2 must write another word: with two words the
-    // waves could read different values and enter different barriers.
+    // Flag words rotate over three iterations: iteration t's commit (after its
+    // barrier) writes word t % 3, iteration t+1 reads it after its own barrier
+    // and serves it, and every wave has read it before barrier t+2. (Two
+    // words would do since every commit follows a barrier; the third keeps
+    // a written word apart from any being read with room to spare.)
     const int par = tile % 3, prev = (tile + 2) % 3;
     float q0 = 0.0f, q1 = 0.0f, q2 = 0.0f, q3 = 0.0f;
     if (mine)
-      q0 = half_step(TrueT{}, TrueT{}, TrueT{}, TrueT{}, lds_k[cur], 1, lds_k[cur], 2, accB, accA, filter_compute);
-    else filter_compute();
-    filter_commit(par);  // the previous tile's keys 64..127
+      q0 = half_step(TrueT{}, TrueT{}, TrueT{}, TrueT{}, lds_k[cur], 1, lds_k[cur], 2, accB, accA, filter_compute_a);
+    else filter_compute_a();
     if (mine) {
       q1 = half_step(TrueT{}, TrueT{}, TrueT{}, TrueT{}, lds_k[cur], 2, lds_k[cur], 3, accA, accB, no_side);
       pend_p0 = q0;
@@ -607,7 +628,7 @@ void indexer_prefill_kernel(IndexerParams p) {
     // this wave's load of tile+1 (issued one iteration ago) must have landed
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    filter_commit(par);  // keys 0..63
+    filter_commit(par);  // the previous tile's keys 64..127 and this tile's 0..63
     // The flags raised by the previous iteration's commits are visible now;
     // read them during the next quarter and serve them after it (the word is
     // next written two iterations later, after the next barrier).
@@ -624,15 +645,15 @@ void indexer_prefill_kernel(IndexerParams p) {
       pend_p0 = q2;
       pend_p1 = q3;
       pend_ksc = ksc1;
-      pend_base = base + kTileKeys;
-      pend_end = kend;
+      pend_a_base = base + kTileKeys;
+      pend_a_end = kend;
     } else {
       read_flags();
     }
     coop_shrinks(uniform_u(flags_v), prev);
   };
   for (int tile = 0; tile < n_tiles; ++tile) iteration(tile);
-  filter_compute();
+  filter_compute_a();
   __syncthreads();
   filter_commit(n_tiles % 3);
   __syncthreads();
