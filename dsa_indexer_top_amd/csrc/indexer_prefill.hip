@@ -600,8 +600,12 @@ void indexer_prefill_kernel(IndexerParams p) {
     const bool mine_next = more && base + kIterKeys < kend;
     float ksc0 = 1.0f, ksc1 = 1.0f;
     if constexpr (FP8) {
-      ksc0 = (mine && base + lane < kend) ? kscale[base + lane] : 0.0f;
-      ksc1 = (mine && base + kTileKeys + lane < kend) ? kscale[base + kTileKeys + lane] : 0.0f;
+      // unconditional loads, clamped into the row's n_k scales (no exec-mask
+      // branch); keys past kend get scale 0
+      const int i0 = base + lane, i1 = base + kTileKeys + lane;
+      const float s0 = kscale[min(i0, p.n_k - 1)], s1 = kscale[min(i1, p.n_k - 1)];
+      ksc0 = (mine && i0 < kend) ? s0 : 0.0f;
+      ksc1 = (mine && i1 < kend) ? s1 : 0.0f;
     }
     // Flag words rotate over three iterations: iteration t's commit (after its
     // barrier) writes word t % 3, iteration t+1 reads it after its own barrier
