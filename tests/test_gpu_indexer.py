@@ -175,3 +175,28 @@ def test_decode_fp8(dsa):
     say("decode fp8")
     inp = make_indexer_inputs(2, 1, 4000, 64, 128, config=24, dtype="fp8")
     check_indexer(dsa, inp, 512)
+
+
+@pytest.mark.parametrize("L,topk,H,D", [(3000, 8, 4, 32), (9000, 2048, 16, 64)])
+def test_prefill_every_key_accepted(dsa, L, topk, H, D):
+    """score(t, s) = H * s exactly (q = (256, 1, 0, ..), k_s = (s // 256,
+    s % 256, 0, ..), w = 1), rising with the key index: every key passes the
+    row's threshold, so each commit appends the most it can and the list is
+    flagged and shrunk as often as the list margin allows. Each row's top-k
+    is its k latest keys, newest first."""
+    say(f"prefill every key accepted L={L} k={topk}")
+    inp = make_int_indexer_inputs(1, L, L, H, D, seed=14)
+    inp.q.zero_()
+    inp.q[..., 0] = 256
+    inp.q[..., 1] = 1
+    s = torch.arange(L)
+    inp.k.zero_()
+    inp.k[0, :, 0] = (s // 256).to(inp.k.dtype)
+    inp.k[0, :, 1] = (s % 256).to(inp.k.dtype)
+    inp.w.fill_(1.0)
+    rows = [0, 1, topk - 1, topk, topk + 1, L // 2, L - 2, L - 1]
+    rows += list(np.random.default_rng(3).choice(L, 24, replace=False))
+    r, _ = check_indexer(dsa, inp, topk, rows=sorted(set(int(x) for x in rows)), exact=True)
+    t = np.arange(L)[:, None]
+    j = np.arange(topk)[None, :]
+    assert np.array_equal(r.idx.cpu().numpy()[0], np.where(t - j >= 0, t - j, -1))
