@@ -200,3 +200,14 @@ def test_prefill_every_key_accepted(dsa, L, topk, H, D):
     t = np.arange(L)[:, None]
     j = np.arange(topk)[None, :]
     assert np.array_equal(r.idx.cpu().numpy()[0], np.where(t - j >= 0, t - j, -1))
+
+
+@pytest.mark.parametrize("shape,topk,cfg", [
+    ((1, 130, 700, 64, 128), 32, 15),     # chunked prefill: queries are the last 130 of 700
+    ((2, 333, 333, 64, 128), 100, 16),    # two batch entries
+    ((1, 129, 1000, 16, 64), 200, 17),    # d = 64, chunk ending in a ragged tile
+])
+def test_prefill_fp8_chunked_and_batched(dsa, shape, topk, cfg):
+    say(f"prefill fp8 {shape} k={topk}")
+    inp = make_indexer_inputs(*shape, config=cfg, dtype="fp8")
+    check_indexer(dsa, inp, topk)
