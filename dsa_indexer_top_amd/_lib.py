@@ -27,6 +27,8 @@ EXPORTS = (
     "dsa_indexer_scores_topk",
     "dsa_sparse_attn",
     "dsa_layer_stack_run",
+    "dsa_chunked_stack_workspace_size",
+    "dsa_layer_stack_run_chunked",
     "dsa_quantize_fp8_rows",
     "dsa_paged_indexer_topk",
     "dsa_paged_sparse_attn",
@@ -118,6 +120,10 @@ def load() -> ctypes.CDLL:
     lib.dsa_sparse_attn.argtypes = [POINTER(AttnArgs), c_void_p]
     lib.dsa_layer_stack_run.restype = c_int32
     lib.dsa_layer_stack_run.argtypes = [POINTER(StackArgs), c_char_p, c_int32, c_void_p]
+    lib.dsa_chunked_stack_workspace_size.restype = c_int32
+    lib.dsa_chunked_stack_workspace_size.argtypes = [POINTER(StackArgs), c_int32, POINTER(c_size_t)]
+    lib.dsa_layer_stack_run_chunked.restype = c_int32
+    lib.dsa_layer_stack_run_chunked.argtypes = [POINTER(StackArgs), c_int32, c_char_p, c_int32, c_void_p]
     lib.dsa_paged_indexer_topk.restype = c_int32
     lib.dsa_paged_indexer_topk.argtypes = [POINTER(IndexerArgs), POINTER(PagedKVArgs), c_void_p]
     lib.dsa_paged_sparse_attn.restype = c_int32

@@ -64,17 +64,46 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"indexer inputs must be bfloat16 or float8_e4m3fn, got {t.dtype}")
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, shape=None):
+    """Type, dtype, rank, exact shape and contiguity of a caller tensor. The C
+    ABI carries no shapes, so every tensor a kernel reads or writes is checked
+    here; devices are checked afterwards by _on_gpu (shape errors first, so
+    they are reported the same way on a host without a GPU)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(*named):
+    """Every given (name, tensor) pair (None tensors skipped) is a GPU tensor,
+    all on one device; returns that device."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    return dev
+
+
+def _opt_out(spec, name: str, dtype, shape):
+    """An optional output argument: True (allocate later), False/None (absent)
+    or a caller tensor, which must have exactly this dtype and shape."""
+    if spec is True or spec is False or spec is None:
+        return spec
+    _need(spec, name, dtype=dtype, shape=shape)
+    return spec
 
 
 def indexer_args(B, n_q, n_k, pos_offset, H, D, topk, dtype_code) -> L.IndexerArgs:
@@ -112,12 +141,16 @@ def attn_workspace_size(B, n_q, n_k, H, D, topk, pos_offset=None) -> int:
 
 
 def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
-    if nbytes == 0:
-        return given
     if given is not None:
+        _need(given, "workspace")
+        _on_gpu(("workspace", given))
+        if given.device != device:
+            raise ValueError(f"workspace is on {given.device}, the other tensors on {device}")
         if given.numel() * given.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return given
+    if nbytes == 0:
+        return None
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
@@ -146,26 +179,25 @@ def indexer_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk:
     B, n_q, H, D = q.shape
     _need(k, "k", dtype=q.dtype, ndim=3)
     n_k = k.shape[1]
-    if k.shape[0] != B or k.shape[2] != D:
-        raise ValueError("k must be [B, n_k, D]")
-    _need(w, "w", dtype=torch.float32, ndim=3)
-    if tuple(w.shape) != (B, n_q, H):
-        raise ValueError("w must be [B, n_q, H]")
+    _need(k, "k", shape=(B, n_k, D))
+    _need(w, "w", dtype=torch.float32, shape=(B, n_q, H))
     code = _dtype_code(q)
     if code == L.DSA_FP8_E4M3FN:
-        _need(q_scale, "q_scale", dtype=torch.float32, ndim=2)
-        _need(k_scale, "k_scale", dtype=torch.float32, ndim=2)
-        if tuple(q_scale.shape) != (B, n_q) or tuple(k_scale.shape) != (B, n_k):
-            raise ValueError("q_scale must be [B, n_q] and k_scale [B, n_k]")
+        _need(q_scale, "q_scale", dtype=torch.float32, shape=(B, n_q))
+        _need(k_scale, "k_scale", dtype=torch.float32, shape=(B, n_k))
+    elif q_scale is not None or k_scale is not None:
+        raise ValueError("q_scale and k_scale are for fp8 inputs only")
     if pos_offset is None:
         pos_offset = n_k - n_q
-    dev = q.device
+    if out_idx is not None:
+        _need(out_idx, "out_idx", dtype=torch.int32, shape=(B, n_q, topk))
+    out_scores = _opt_out(out_scores, "out_scores", torch.float32, (B, n_q, topk))
+    debug_full_scores = _opt_out(debug_full_scores, "debug_full_scores", torch.float32, (B, n_q, n_k))
+    dev = _on_gpu(("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale), ("out_idx", out_idx),
+                  ("out_scores", out_scores if isinstance(out_scores, torch.Tensor) else None),
+                  ("debug_full_scores", debug_full_scores if isinstance(debug_full_scores, torch.Tensor) else None))
     if out_idx is None:
         out_idx = torch.empty((B, n_q, topk), dtype=torch.int32, device=dev)
-    else:
-        _need(out_idx, "out_idx", dtype=torch.int32)
-        if tuple(out_idx.shape) != (B, n_q, topk):
-            raise ValueError("out_idx must be [B, n_q, topk]")
     sc = None
     if out_scores is True:
         sc = torch.empty((B, n_q, topk), dtype=torch.float32, device=dev)
@@ -200,21 +232,21 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Te
     _need(q, "q", dtype=torch.bfloat16, ndim=4)
     B, n_q, H, D = q.shape
     _need(k, "k", dtype=torch.bfloat16, ndim=3)
-    _need(v, "v", dtype=torch.bfloat16, ndim=3)
     n_k = k.shape[1]
-    if tuple(k.shape) != (B, n_k, D) or tuple(v.shape) != (B, n_k, D):
-        raise ValueError("k and v must be [B, n_k, D]")
+    _need(k, "k", shape=(B, n_k, D))
+    _need(v, "v", dtype=torch.bfloat16, shape=(B, n_k, D))
     _need(idx, "idx", dtype=torch.int32, ndim=3)
-    if idx.shape[0] != B or idx.shape[1] != n_q:
-        raise ValueError("idx must be [B, n_q, topk]")
     topk = idx.shape[2]
+    _need(idx, "idx", shape=(B, n_q, topk))
     if pos_offset is None:
         pos_offset = n_k - n_q
-    dev = q.device
+    if out is not None:
+        _need(out, "out", dtype=torch.bfloat16, shape=(B, n_q, H, D))
+    lse = _opt_out(lse, "lse", torch.float32, (B, n_q, H))
+    dev = _on_gpu(("q", q), ("k", k), ("v", v), ("idx", idx), ("out", out),
+                  ("lse", lse if isinstance(lse, torch.Tensor) else None))
     if out is None:
         out = torch.empty((B, n_q, H, D), dtype=torch.bfloat16, device=dev)
-    else:
-        _need(out, "out", dtype=torch.bfloat16)
     lse_t = None
     if lse is True:
         lse_t = torch.empty((B, n_q, H), dtype=torch.float32, device=dev)
@@ -246,6 +278,7 @@ class PagedKV:
         _need(block_table, "block_table", dtype=torch.int32, ndim=2)
         if block_table.shape[0] != seq_lens.shape[0]:
             raise ValueError("block_table must be [B, max_pages]")
+        self.device = _on_gpu(("seq_lens", seq_lens), ("block_table", block_table))
         self.seq_lens, self.block_table = seq_lens, block_table
         self.page_size, self.num_pages, self.max_seq_len = int(page_size), int(num_pages), int(max_seq_len)
         self.B, self.max_pages = block_table.shape
@@ -256,9 +289,13 @@ class PagedKV:
         a.seq_lens, a.block_table = _ptr(seq_lens), _ptr(block_table)
         self.args = a
 
-    def check_pool(self, pool: torch.Tensor, name: str, row_shape):
+    def check_pool(self, pool: torch.Tensor, name: str, row_shape, dtype=None):
+        _need(pool, name, dtype=dtype)
         if tuple(pool.shape) != (self.num_pages, self.page_size, *row_shape):
             raise ValueError(f"{name} must be [num_pages, page_size, {', '.join(map(str, row_shape))}]")
+        _on_gpu((name, pool))
+        if pool.device != self.device:
+            raise ValueError(f"{name} is on {pool.device}, the cache layout on {self.device}")
 
 
 def paged_indexer_topk(q: torch.Tensor, k_pool: torch.Tensor, w: torch.Tensor, topk: int, kv: PagedKV, *,
@@ -274,26 +311,26 @@ def paged_indexer_topk(q: torch.Tensor, k_pool: torch.Tensor, w: torch.Tensor, t
     B, n_q, H, D = q.shape
     if n_q != 1 or B != kv.B:
         raise ValueError("q must be [B, 1, H, D] with B = kv.B")
-    _need(k_pool, "k_pool", dtype=q.dtype)
-    kv.check_pool(k_pool, "k_pool", (D,))
-    _need(w, "w", dtype=torch.float32, ndim=3)
-    if tuple(w.shape) != (B, 1, H):
-        raise ValueError("w must be [B, 1, H]")
+    kv.check_pool(k_pool, "k_pool", (D,), dtype=q.dtype)
+    _need(w, "w", dtype=torch.float32, shape=(B, 1, H))
     code = _dtype_code(q)
     if code == L.DSA_FP8_E4M3FN:
-        _need(q_scale, "q_scale", dtype=torch.float32, ndim=2)
-        _need(k_scale_pool, "k_scale_pool", dtype=torch.float32, ndim=2)
-        kv.check_pool(k_scale_pool, "k_scale_pool", ())
-        if tuple(q_scale.shape) != (B, 1):
-            raise ValueError("q_scale must be [B, 1]")
-    dev = q.device
+        _need(q_scale, "q_scale", dtype=torch.float32, shape=(B, 1))
+        kv.check_pool(k_scale_pool, "k_scale_pool", (), dtype=torch.float32)
+    elif q_scale is not None or k_scale_pool is not None:
+        raise ValueError("q_scale and k_scale_pool are for fp8 inputs only")
     n_k = kv.max_seq_len
+    if out_idx is not None:
+        _need(out_idx, "out_idx", dtype=torch.int32, shape=(B, 1, topk))
+    out_scores = _opt_out(out_scores, "out_scores", torch.float32, (B, 1, topk))
+    debug_full_scores = _opt_out(debug_full_scores, "debug_full_scores", torch.float32, (B, 1, n_k))
+    dev = _on_gpu(("q", q), ("w", w), ("q_scale", q_scale), ("out_idx", out_idx),
+                  ("out_scores", out_scores if isinstance(out_scores, torch.Tensor) else None),
+                  ("debug_full_scores", debug_full_scores if isinstance(debug_full_scores, torch.Tensor) else None))
+    if dev != kv.device:
+        raise ValueError(f"q is on {dev}, the cache layout on {kv.device}")
     if out_idx is None:
         out_idx = torch.empty((B, 1, topk), dtype=torch.int32, device=dev)
-    else:
-        _need(out_idx, "out_idx", dtype=torch.int32)
-        if tuple(out_idx.shape) != (B, 1, topk):
-            raise ValueError("out_idx must be [B, 1, topk]")
     sc = torch.empty((B, 1, topk), dtype=torch.float32, device=dev) if out_scores is True else (
         out_scores if isinstance(out_scores, torch.Tensor) else None)
     full = torch.full((B, 1, n_k), float("nan"), dtype=torch.float32, device=dev) if debug_full_scores is True \
@@ -324,13 +361,16 @@ def paged_sparse_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
     if n_q != 1 or B != kv.B:
         raise ValueError("q must be [B, 1, H, D] with B = kv.B")
     for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool")):
-        _need(t, nm, dtype=torch.bfloat16)
-        kv.check_pool(t, nm, (D,))
+        kv.check_pool(t, nm, (D,), dtype=torch.bfloat16)
     _need(idx, "idx", dtype=torch.int32, ndim=3)
-    if idx.shape[0] != B or idx.shape[1] != 1:
-        raise ValueError("idx must be [B, 1, topk]")
     topk = idx.shape[2]
-    dev = q.device
+    _need(idx, "idx", shape=(B, 1, topk))
+    if out is not None:
+        _need(out, "out", dtype=torch.bfloat16, shape=(B, 1, H, D))
+    lse = _opt_out(lse, "lse", torch.float32, (B, 1, H))
+    dev = _on_gpu(("q", q), ("idx", idx), ("out", out), ("lse", lse if isinstance(lse, torch.Tensor) else None))
+    if dev != kv.device:
+        raise ValueError(f"q is on {dev}, the cache layout on {kv.device}")
     n_k = kv.max_seq_len
     if out is None:
         out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=dev)
@@ -353,11 +393,13 @@ def paged_append_rows(src: torch.Tensor, pool: torch.Tensor, kv: PagedKV, stream
     """dsa_paged_append_rows: src [B, ...] (one row per request) goes to each
     request's last position, seq_lens[b] - 1, of pool [num_pages, page_size, ...]."""
     _need(src, "src")
-    _need(pool, "pool", dtype=src.dtype)
     B = src.shape[0]
     if B != kv.B:
         raise ValueError("src must have one row per request")
-    kv.check_pool(pool, "pool", tuple(src.shape[1:]))
+    kv.check_pool(pool, "pool", tuple(src.shape[1:]), dtype=src.dtype)
+    _on_gpu(("src", src), ("pool", pool))
+    if src.device != kv.device:
+        raise ValueError(f"src is on {src.device}, the cache layout on {kv.device}")
     row_bytes = (src.numel() // B) * src.element_size()
     _check(L.load().dsa_paged_append_rows(_ptr(src), B, row_bytes, _ptr(pool), ctypes.byref(kv.args),
                                           _stream(stream)))
@@ -369,12 +411,11 @@ def topk_overlap(idx: torch.Tensor, n_k: int, *, out: Optional[torch.Tensor] = N
     of tokens both layers selected. The overlap ratio is inter[a][b] / inter[a][a]."""
     _need(idx, "idx", dtype=torch.int32, ndim=3)
     n_layers, rows, topk = idx.shape
+    if out is not None:
+        _need(out, "out", dtype=torch.int64, shape=(n_layers, n_layers))
+    dev = _on_gpu(("idx", idx), ("out", out))
     if out is None:
-        out = torch.empty((n_layers, n_layers), dtype=torch.int64, device=idx.device)
-    else:
-        _need(out, "out", dtype=torch.int64)
-        if tuple(out.shape) != (n_layers, n_layers):
-            raise ValueError("out must be [n_layers, n_layers]")
+        out = torch.empty((n_layers, n_layers), dtype=torch.int64, device=dev)
     _check(L.load().dsa_topk_overlap(_ptr(idx), n_layers, rows, topk, int(n_k), _ptr(out), _stream(stream)))
     return out
 
@@ -403,16 +444,21 @@ def quantize_fp8_rows(x: torch.Tensor, *, out: Optional[torch.Tensor] = None,
     -> pass x.view(B, n_q, H * D); k_idx [B, n_k, D] as is). Returns (codes as
     float8_e4m3fn with x's shape, scale fp32 with x's shape minus the last dim)."""
     _need(x, "x", dtype=torch.bfloat16)
+    if x.dim() < 1:
+        raise ValueError("x must have at least one dim")
     cols = x.shape[-1]
     rows = x.numel() // cols if cols else 0
+    if out is not None:
+        _need(out, "out", dtype=torch.float8_e4m3fn, shape=x.shape)
+    if scale is not None:
+        _need(scale, "scale", dtype=torch.float32)
+        if scale.numel() != rows:
+            raise ValueError(f"scale must have one entry per row ({rows}), got {scale.numel()}")
+    dev = _on_gpu(("x", x), ("out", out), ("scale", scale))
     if out is None:
-        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev)
     if scale is None:
-        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _need(out, "out", dtype=torch.float8_e4m3fn)
-    _need(scale, "scale", dtype=torch.float32)
-    if tuple(out.shape) != tuple(x.shape) or scale.numel() != rows:
-        raise ValueError("out must have x's shape and scale one entry per row")
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=dev)
     _check(L.load().dsa_quantize_fp8_rows(_ptr(x), rows, cols, _ptr(out), _ptr(scale), _stream(stream)))
     return out, scale
 
@@ -444,38 +490,64 @@ class LayerStack:
 
     def __init__(self, layers: List[dict], topk: int, *, scale: float = 0.0,
                  pos_offset: Optional[int] = None, lse: bool = False, shared_out: bool = False,
-                 events: bool = False, kv: Optional[PagedKV] = None):
+                 events: bool = False, kv: Optional[PagedKV] = None, chunk_rows: Optional[int] = None):
         """kv: a PagedKV for one decode step over paged caches (every layer's
-        k_idx, k_scale, k and v are then page pools and n_q must be 1)."""
+        k_idx, k_scale, k and v are then page pools and n_q must be 1).
+        chunk_rows: prefill the rows in chunks of this many (one sequence,
+        B = 1; dsa_layer_stack_run_chunked): the index buffer then holds one
+        chunk's rows and the workspace is sized for one chunk."""
+        if not layers:
+            raise ValueError("layers is empty")
         l0 = layers[0]
+        _need(l0["q_idx"], "layers[0].q_idx", ndim=4)
+        _need(l0["q"], "layers[0].q", dtype=torch.bfloat16, ndim=4)
         B, n_q, H_I, D_I = l0["q_idx"].shape
-        n_k = l0["k_idx"].shape[1] if kv is None else kv.max_seq_len
         _, _, H, D = l0["q"].shape
-        if kv is not None:
-            if n_q != 1:
-                raise ValueError("a paged stack is one decode step: n_q must be 1")
-            for i, ly in enumerate(layers):
-                kv.check_pool(ly["k_idx"], f"layers[{i}].k_idx", (D_I,))
-                kv.check_pool(ly["k"], f"layers[{i}].k", (D,))
-                kv.check_pool(ly["v"], f"layers[{i}].v", (D,))
-                if ly.get("k_scale") is not None:
-                    kv.check_pool(ly["k_scale"], f"layers[{i}].k_scale", ())
-        self.kv = kv
-        if pos_offset is None:
-            pos_offset = n_k - n_q
         code = _dtype_code(l0["q_idx"])
         fp8 = code == L.DSA_FP8_E4M3FN
-        dev = l0["q"].device
+        if kv is None:
+            _need(l0["k_idx"], "layers[0].k_idx", ndim=3)
+            n_k = l0["k_idx"].shape[1]
+        else:
+            n_k = kv.max_seq_len
+            if n_q != 1:
+                raise ValueError("a paged stack is one decode step: n_q must be 1")
+        if chunk_rows is not None and (kv is not None or B != 1 or int(chunk_rows) < 1 or events):
+            raise ValueError("chunk_rows needs one flat-cache sequence (B = 1), chunk_rows >= 1 and no "
+                             "per-layer events")
+        named = []
         for i, ly in enumerate(layers):
-            _need(ly["q_idx"], f"layers[{i}].q_idx", dtype=l0["q_idx"].dtype)
-            _need(ly["k_idx"], f"layers[{i}].k_idx", dtype=l0["q_idx"].dtype)
-            _need(ly["w"], f"layers[{i}].w", dtype=torch.float32)
-            for nm in ("q", "k", "v"):
-                _need(ly[nm], f"layers[{i}].{nm}", dtype=torch.bfloat16)
-            if tuple(ly["q_idx"].shape) != (B, n_q, H_I, D_I) or tuple(ly["q"].shape) != (B, n_q, H, D):
-                raise ValueError(f"layer {i}: shapes differ from layer 0")
+            pre = f"layers[{i}]."
+            _need(ly["q_idx"], pre + "q_idx", dtype=l0["q_idx"].dtype, shape=(B, n_q, H_I, D_I))
+            _need(ly["w"], pre + "w", dtype=torch.float32, shape=(B, n_q, H_I))
+            _need(ly["q"], pre + "q", dtype=torch.bfloat16, shape=(B, n_q, H, D))
+            if kv is None:
+                _need(ly["k_idx"], pre + "k_idx", dtype=l0["q_idx"].dtype, shape=(B, n_k, D_I))
+                _need(ly["k"], pre + "k", dtype=torch.bfloat16, shape=(B, n_k, D))
+                _need(ly["v"], pre + "v", dtype=torch.bfloat16, shape=(B, n_k, D))
+            else:
+                kv.check_pool(ly["k_idx"], pre + "k_idx", (D_I,), dtype=l0["q_idx"].dtype)
+                kv.check_pool(ly["k"], pre + "k", (D,), dtype=torch.bfloat16)
+                kv.check_pool(ly["v"], pre + "v", (D,), dtype=torch.bfloat16)
+            if fp8:
+                _need(ly.get("q_scale"), pre + "q_scale", dtype=torch.float32, shape=(B, n_q))
+                if kv is None:
+                    _need(ly.get("k_scale"), pre + "k_scale", dtype=torch.float32, shape=(B, n_k))
+                else:
+                    kv.check_pool(ly.get("k_scale"), pre + "k_scale", (), dtype=torch.float32)
+            elif ly.get("q_scale") is not None or ly.get("k_scale") is not None:
+                raise ValueError(f"layer {i}: q_scale/k_scale are for fp8 inputs only")
+            named += [(pre + nm, ly.get(nm)) for nm in ("q_idx", "k_idx", "w", "q_scale", "k_scale", "q", "k", "v")]
+        dev = _on_gpu(*named)
+        if kv is not None and dev != kv.device:
+            raise ValueError(f"the layers are on {dev}, the cache layout on {kv.device}")
+        self.kv = kv
+        self.chunk_rows = None if chunk_rows is None else int(chunk_rows)
+        if pos_offset is None:
+            pos_offset = n_k - n_q
         self.layers = layers
-        self.idx_buf = torch.empty((B, n_q, topk), dtype=torch.int32, device=dev)
+        buf_rows = n_q if self.chunk_rows is None else min(self.chunk_rows, n_q)
+        self.idx_buf = torch.empty((B, buf_rows, topk), dtype=torch.int32, device=dev)
         if shared_out:
             o = torch.empty((B, n_q, H, D), dtype=torch.bfloat16, device=dev)
             self.outs = [o] * len(layers)
@@ -508,7 +580,10 @@ class LayerStack:
             self._keep.append(ev)
             a.layer_events = ctypes.cast(ev, ctypes.c_void_p)
         n = ctypes.c_size_t(0)
-        _check(L.load().dsa_stack_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+        if self.chunk_rows is None:
+            _check(L.load().dsa_stack_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+        else:
+            _check(L.load().dsa_chunked_stack_workspace_size(ctypes.byref(a), self.chunk_rows, ctypes.byref(n)))
         self.workspace = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
         a.workspace = _ptr(self.workspace)
         a.workspace_bytes = self.workspace.numel()
@@ -516,7 +591,10 @@ class LayerStack:
 
     def run(self, pattern: Optional[str] = None, freq: int = 0, stream=None):
         pat = None if pattern is None else pattern.encode()
-        if self.kv is None:
+        if self.chunk_rows is not None:
+            _check(L.load().dsa_layer_stack_run_chunked(ctypes.byref(self.args), self.chunk_rows, pat, int(freq),
+                                                        _stream(stream)))
+        elif self.kv is None:
             _check(L.load().dsa_layer_stack_run(ctypes.byref(self.args), pat, int(freq), _stream(stream)))
         else:
             _check(L.load().dsa_paged_layer_stack_run(ctypes.byref(self.args), ctypes.byref(self.kv.args), pat,

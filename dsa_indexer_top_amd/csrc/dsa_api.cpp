@@ -470,6 +470,123 @@ dsa_status dsa_layer_stack_run(const dsa_stack_args* a, const char* pattern, int
   return stack_run(a, nullptr, pattern, freq, stream, "layer_stack_run");
 }
 
+// The stack arguments of chunk [c0, c1) of a chunked prefill: the query rows'
+// pointers advanced to row c0 (B = 1, dense rows), the keys cut to the
+// chunk's last position, and the caller's per-chunk index buffer. The
+// per-layer pointer arrays live in `store` (5 + 2 arrays of n_layers).
+static dsa_stack_args chunk_args(const dsa_stack_args* a, int c0, int c1, std::vector<const void*>& store) {
+  const int n = a->n_layers;
+  const dsa_indexer_args& ix = a->indexer;
+  const dsa_attn_args& at = a->attn;
+  const bool fp8 = ix.dtype == DSA_FP8_E4M3FN;
+  const size_t qi_row = (size_t)ix.n_heads * ix.head_dim * (fp8 ? 1 : 2);
+  const size_t q_row = (size_t)at.n_heads * at.head_dim * 2;
+  store.assign((size_t)7 * n, nullptr);
+  const void** qi = &store[0];
+  const void** w = &store[(size_t)n];
+  const void** qs = &store[(size_t)2 * n];
+  const void** q = &store[(size_t)3 * n];
+  const void** out = &store[(size_t)4 * n];
+  const void** lse = &store[(size_t)5 * n];
+  for (int l = 0; l < n; ++l) {
+    qi[l] = a->q_idx[l] ? (const char*)a->q_idx[l] + (size_t)c0 * qi_row : nullptr;
+    w[l] = a->w[l] ? a->w[l] + (size_t)c0 * ix.n_heads : nullptr;
+    if (a->q_scale) qs[l] = a->q_scale[l] ? a->q_scale[l] + c0 : nullptr;
+    q[l] = a->q[l] ? (const char*)a->q[l] + (size_t)c0 * q_row : nullptr;
+    out[l] = a->out[l] ? (char*)a->out[l] + (size_t)c0 * q_row : nullptr;
+    if (a->lse) lse[l] = a->lse[l] ? a->lse[l] + (size_t)c0 * at.n_heads : nullptr;
+  }
+  dsa_stack_args c = *a;
+  c.indexer.n_q = c.attn.n_q = c1 - c0;
+  c.indexer.q_pos_offset = c.attn.q_pos_offset = ix.q_pos_offset + c0;
+  c.indexer.n_k = c.attn.n_k = ix.q_pos_offset + c1;
+  c.q_idx = qi;
+  c.w = (const float* const*)w;
+  c.q_scale = a->q_scale ? (const float* const*)qs : nullptr;
+  c.q = q;
+  c.out = (void* const*)out;
+  c.lse = a->lse ? (float* const*)lse : nullptr;
+  c.layer_events = nullptr;
+  return c;
+}
+
+static dsa_status check_chunked(const dsa_stack_args* a, int32_t chunk_rows, const char* what) {
+  dsa_status st = check_stack_shape(a, what);
+  if (st != DSA_OK) return st;
+  if (a->indexer.B != 1)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: chunked prefill takes one sequence (B = 1), got B = %d", what, a->indexer.B);
+  if (chunk_rows < 1) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: chunk_rows=%d must be >= 1", what, chunk_rows);
+  if (a->layer_events) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: layer_events must be NULL (per-layer events do not span chunks)", what);
+  return DSA_OK;
+}
+
+// Workspace of the largest chunk shape: a full chunk and the ragged last one
+// (the attention split, hence its partials, depends on the row count; a
+// one-row chunk takes the decode path).
+static size_t chunked_ws(const dsa_stack_args* a, int32_t chunk_rows) {
+  const int n_q = a->indexer.n_q;
+  const int full = std::min(chunk_rows, n_q);
+  const int last = n_q % full;
+  size_t need = 0;
+  for (int rows : {full, last}) {
+    if (rows < 1) continue;
+    dsa_stack_args c = *a;
+    c.indexer.n_q = c.attn.n_q = rows;
+    c.indexer.q_pos_offset = c.attn.q_pos_offset = a->indexer.n_k - rows;  // the largest key count
+    need = std::max(need, stack_ws(&c));
+  }
+  return need;
+}
+
+dsa_status dsa_chunked_stack_workspace_size(const dsa_stack_args* a, int32_t chunk_rows, size_t* bytes) {
+  const char* what = "chunked_stack_workspace_size";
+  dsa_status st = check_chunked(a, chunk_rows, what);
+  if (st != DSA_OK) return st;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARGUMENT, "%s: bytes is NULL", what);
+  *bytes = chunked_ws(a, chunk_rows);
+  return ok();
+}
+
+dsa_status dsa_layer_stack_run_chunked(const dsa_stack_args* a, int32_t chunk_rows, const char* pattern, int32_t freq,
+                                       void* stream) {
+  const char* what = "layer_stack_run_chunked";
+  dsa_status st = check_chunked(a, chunk_rows, what);
+  if (st != DSA_OK) return st;
+  const int n_q = a->indexer.n_q;
+  std::string P((size_t)a->n_layers + 1, '\0');
+  st = dsa_resolve_pattern(a->n_layers, pattern, freq, &P[0]);
+  if (st != DSA_OK) return st;
+  if (!a->q_idx || !a->k_idx || !a->w || !a->q || !a->k || !a->v || !a->out || !a->idx_buf)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: per-layer arrays and idx_buf are required", what);
+  st = check_workspace(a->workspace, a->workspace_bytes, chunked_ws(a, chunk_rows), what);
+  if (st != DSA_OK) return st;
+  // every chunk's arguments are validated before the first one is enqueued
+  std::vector<const void*> store;
+  for (int c0 = 0; c0 < n_q; c0 += chunk_rows) {
+    const int c1 = std::min(n_q, c0 + chunk_rows);
+    dsa_stack_args c = chunk_args(a, c0, c1, store);
+    st = check_stack_shape(&c, what);
+    if (st != DSA_OK) return fail(st, "%s (chunk at row %d)", dsa_last_error(), c0);
+    if (c0 > 0) continue;
+    // pointers and alignment are the same for every chunk up to the row offsets
+    const bool fp8 = c.indexer.dtype == DSA_FP8_E4M3FN;
+    for (int l = 0; l < c.n_layers; ++l) {
+      st = check_indexer_ptrs(&c.indexer, c.q_idx[l], c.k_idx[l], c.w[l], fp8 ? c.q_scale[l] : nullptr,
+                              fp8 ? c.k_scale[l] : nullptr, c.idx_buf, what);
+      if (st != DSA_OK) return fail(st, "%s (layer %d)", dsa_last_error(), l);
+      st = check_attn_ptrs(c.q[l], c.k[l], c.v[l], c.idx_buf, c.out[l], c.lse ? c.lse[l] : nullptr, what);
+      if (st != DSA_OK) return fail(st, "%s (layer %d)", dsa_last_error(), l);
+    }
+  }
+  for (int c0 = 0; c0 < n_q; c0 += chunk_rows) {
+    const int c1 = std::min(n_q, c0 + chunk_rows);
+    dsa_stack_args c = chunk_args(a, c0, c1, store);
+    st = stack_run(&c, nullptr, P.c_str(), 0, stream, what);
+    if (st != DSA_OK) return fail(st, "%s (chunk at row %d)", dsa_last_error(), c0);
+  }
+  return ok();
+}
+
 // Validates the paged layout for decode shapes (n_q == 1, n_k == max_seq_len)
 // and fills the kernels' view of it.
 static dsa_status check_paged(const dsa_paged_kv* kv, int B, int n_q, int n_k, int64_t row_bytes, const char* what,

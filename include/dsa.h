@@ -238,6 +238,33 @@ dsa_status dsa_sparse_attn(const dsa_attn_args *args, void *stream);
 dsa_status dsa_layer_stack_run(const dsa_stack_args *args, const char *pattern,
                                int32_t index_topk_freq, void *stream);
 
+/* Chunked prefill of one sequence through the layer stack: a long prompt is
+ * prefilled in chunks of query rows over the keys cached so far (the prefill
+ * columns of the paper's Table 1 reach 200K tokens; a serving engine splits
+ * such prompts). args describe the whole prefill of one sequence (B = 1):
+ * n_q query rows at positions q_pos_offset .. q_pos_offset + n_q - 1 over n_k
+ * keys. Chunk c covers rows [c * chunk_rows, min((c + 1) * chunk_rows, n_q))
+ * and runs the whole stack exactly as dsa_layer_stack_run would with those
+ * rows as its queries and the keys up to the chunk's last position (the
+ * cached prefix plus the chunk) as n_k. Each chunk writes its own rows of
+ * out[l] (and lse[l]); the per-layer query inputs (q_idx, w, q_scale, q) are
+ * read at the chunk's rows; k_idx, k_scale, k and v are read as given.
+ * idx_buf is the per-chunk index cache, [chunk_rows, topk] int32: each F
+ * layer of a chunk overwrites its first rows, each S layer reuses them, and
+ * after the call it holds the last chunk's last F layer's indices. The
+ * results equal one dsa_layer_stack_run over all rows: the indices of every
+ * row bit for bit, and the attention outputs bit for bit when every chunk,
+ * like the whole run, has more than 1024 rows (each row is then handled by
+ * one wave in both runs), within rounding otherwise. The workspace
+ * (dsa_chunked_stack_workspace_size) is sized for one chunk, not the whole
+ * prompt. layer_events must be NULL. B != 1, chunk_rows < 1 or
+ * layer_events set: UNSUPPORTED / INVALID_ARGUMENT, before
+ * anything is enqueued; any other error is reported before the first chunk
+ * is enqueued. */
+dsa_status dsa_chunked_stack_workspace_size(const dsa_stack_args *args, int32_t chunk_rows, size_t *bytes);
+dsa_status dsa_layer_stack_run_chunked(const dsa_stack_args *args, int32_t chunk_rows, const char *pattern,
+                                       int32_t index_topk_freq, void *stream);
+
 /* Decode indexer + top-k over a paged, ragged cache. args as for
  * dsa_indexer_scores_topk with n_q = 1 and n_k = kv->max_seq_len (q_pos_offset
  * is ignored: request b's query sits at seq_lens[b] - 1); k and k_scale point

@@ -276,3 +276,156 @@ def test_paged_stack_validation(lib):
     # layout fine, per-layer arrays missing
     assert lib.dsa_paged_layer_stack_run(ctypes.byref(a), ctypes.byref(kv), b"FS", 0, None) == \
         L.DSA_ERR_INVALID_ARGUMENT
+
+
+def _stack_args(B=1, n_q=64, n_k=64, off=0, layers=4):
+    a = L.StackArgs()
+    a.struct_size = ctypes.sizeof(L.StackArgs)
+    a.n_layers = layers
+    a.indexer = indexer_args(B, n_q, n_k, off, 4, 32, 16, L.DSA_BF16)
+    a.attn = attn_args(B, n_q, n_k, off, 4, 64, 16, 0.0)
+    return a
+
+
+def test_chunked_stack_validation(lib):
+    run = lib.dsa_layer_stack_run_chunked
+    a = _stack_args(B=2)
+    assert run(ctypes.byref(a), 16, None, 0, None) == L.DSA_ERR_UNSUPPORTED          # one sequence only
+    a = _stack_args()
+    assert run(ctypes.byref(a), 0, None, 0, None) == L.DSA_ERR_INVALID_ARGUMENT      # chunk_rows < 1
+    assert run(ctypes.byref(a), 16, b"SFFF", 0, None) == L.DSA_ERR_BAD_PATTERN
+    assert run(ctypes.byref(a), 16, b"FSFS", 0, None) == L.DSA_ERR_INVALID_ARGUMENT  # no per-layer arrays
+    a.layer_events = FAKE
+    assert run(ctypes.byref(a), 16, None, 0, None) == L.DSA_ERR_INVALID_ARGUMENT     # events do not span chunks
+    a.layer_events = None
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_chunked_stack_workspace_size(ctypes.byref(a), 0, ctypes.byref(n)) == L.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_chunked_stack_workspace_is_one_chunk(lib):
+    """The chunked workspace covers the largest chunk shape (a full chunk or
+    the ragged last one), not the whole prompt."""
+    def ws(a, rows):
+        n = ctypes.c_size_t(0)
+        assert lib.dsa_chunked_stack_workspace_size(ctypes.byref(a), rows, ctypes.byref(n)) == 0
+        return n.value
+    L_, k = 9000, 16
+    a = _stack_args(n_q=L_, n_k=L_)
+    full = ws(a, L_)
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_stack_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert full == n.value
+    chunk = ws(a, 3000)
+    assert chunk < full
+    one = dict(idx=dsa.indexer_workspace_size(1, 3000, L_, 4, 32, k),
+               attn=dsa.attn_workspace_size(1, 3000, L_, 4, 64, k))
+    assert chunk == max(one.values())
+    # a one-row last chunk takes the decode path: its workspace counts too
+    dec = dsa.indexer_workspace_size(1, 1, L_, 4, 32, k)
+    assert ws(a, 2999) >= dec   # 9000 = 3 * 2999 + 3 rows
+    assert ws(a, 8999) >= dec   # last chunk of one row
+
+
+# ---- the Python binding checks every caller tensor before anything is launched
+import torch  # noqa: E402
+
+
+def _cpu_inputs(B=1, n_q=8, n_k=8, H=4, D=32):
+    return dict(q=torch.zeros(B, n_q, H, D, dtype=torch.bfloat16), k=torch.zeros(B, n_k, D, dtype=torch.bfloat16),
+                w=torch.zeros(B, n_q, H))
+
+
+@pytest.mark.parametrize("bad,msg", [
+    (dict(k=torch.zeros(1, 8, 16, dtype=torch.bfloat16)), "k must have shape"),
+    (dict(w=torch.zeros(1, 8, 5)), "w must have shape"),
+    (dict(w=torch.zeros(1, 8, 4, dtype=torch.float64)), "w must be"),
+    (dict(out_idx=torch.zeros(1, 8, 15, dtype=torch.int32)), "out_idx must have shape"),
+    (dict(out_scores=torch.zeros(1, 8, 17)), "out_scores must have shape"),
+    (dict(debug_full_scores=torch.zeros(1, 8, 9)), "debug_full_scores must have shape"),
+    (dict(debug_full_scores=torch.zeros(1, 8, 8, dtype=torch.float16)), "debug_full_scores must be"),
+    (dict(q_scale=torch.ones(1, 8)), "for fp8 inputs only"),
+    (dict(), "q must be a GPU tensor"),                     # every shape right: the device check fires
+])
+def test_binding_indexer_argument_checks(bad, msg):
+    d = _cpu_inputs()
+    kw = {k: v for k, v in bad.items() if k not in d}
+    d.update({k: v for k, v in bad.items() if k in d})
+    with pytest.raises((ValueError, TypeError), match=msg):
+        dsa.indexer_scores_topk(d["q"], d["k"], d["w"], 16, **kw)
+
+
+@pytest.mark.parametrize("bad,msg", [
+    (dict(v=torch.zeros(1, 9, 64, dtype=torch.bfloat16)), "v must have shape"),
+    (dict(idx=torch.zeros(1, 7, 16, dtype=torch.int32)), "idx must have shape"),
+    (dict(out=torch.zeros(1, 8, 4, 32, dtype=torch.bfloat16)), "out must have shape"),
+    (dict(lse=torch.zeros(1, 8, 5)), "lse must have shape"),
+    (dict(), "q must be a GPU tensor"),
+])
+def test_binding_attention_argument_checks(bad, msg):
+    d = dict(q=torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16), k=torch.zeros(1, 8, 64, dtype=torch.bfloat16),
+             v=torch.zeros(1, 8, 64, dtype=torch.bfloat16), idx=torch.zeros(1, 8, 16, dtype=torch.int32))
+    kw = {k: v for k, v in bad.items() if k not in d}
+    d.update({k: v for k, v in bad.items() if k in d})
+    with pytest.raises((ValueError, TypeError), match=msg):
+        dsa.sparse_attn(d["q"], d["k"], d["v"], d["idx"], **kw)
+
+
+def _layers(n=2, n_q=8, n_k=8, fp8=False):
+    dt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    out = []
+    for _ in range(n):
+        out.append(dict(q_idx=torch.zeros(1, n_q, 4, 32, dtype=dt), k_idx=torch.zeros(1, n_k, 32, dtype=dt),
+                        w=torch.zeros(1, n_q, 4),
+                        q_scale=torch.ones(1, n_q) if fp8 else None, k_scale=torch.ones(1, n_k) if fp8 else None,
+                        q=torch.zeros(1, n_q, 4, 64, dtype=torch.bfloat16),
+                        k=torch.zeros(1, n_k, 64, dtype=torch.bfloat16),
+                        v=torch.zeros(1, n_k, 64, dtype=torch.bfloat16)))
+    return out
+
+
+@pytest.mark.parametrize("layer,name,val,msg", [
+    (1, "k_idx", torch.zeros(1, 9, 32, dtype=torch.bfloat16), r"layers\[1\].k_idx must have shape"),
+    (1, "w", torch.zeros(1, 8, 3), r"layers\[1\].w must have shape"),
+    (1, "v", torch.zeros(1, 8, 32, dtype=torch.bfloat16), r"layers\[1\].v must have shape"),
+    (1, "k", torch.zeros(1, 8, 64, dtype=torch.float32), r"layers\[1\].k must be"),
+    (0, "q_scale", torch.ones(1, 8), "fp8 inputs only"),
+    (1, "q", torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16), "layers.0..q_idx must be a GPU tensor"),
+])
+def test_binding_stack_argument_checks(layer, name, val, msg):
+    ls = _layers()
+    ls[layer][name] = val
+    with pytest.raises((ValueError, TypeError), match=msg):
+        dsa.LayerStack(ls, 16)
+
+
+def test_binding_stack_fp8_scales_checked():
+    ls = _layers(fp8=True)
+    ls[1]["k_scale"] = torch.ones(1, 7)
+    with pytest.raises(ValueError, match=r"layers\[1\].k_scale must have shape"):
+        dsa.LayerStack(ls, 16)
+    ls = _layers(fp8=True)
+    ls[0]["q_scale"] = None
+    with pytest.raises(TypeError, match=r"layers\[0\].q_scale must be a torch.Tensor"):
+        dsa.LayerStack(ls, 16)
+
+
+def test_binding_chunked_stack_arguments():
+    with pytest.raises(ValueError, match="chunk_rows"):
+        dsa.LayerStack(_layers(), 16, chunk_rows=0)
+    with pytest.raises(ValueError, match="chunk_rows"):
+        dsa.LayerStack(_layers(), 16, chunk_rows=4, events=True)
+
+
+def test_binding_other_argument_checks():
+    with pytest.raises(ValueError, match="out must have shape"):
+        dsa.topk_overlap(torch.zeros(3, 2, 4, dtype=torch.int32), 10, out=torch.zeros(3, 2, dtype=torch.int64))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        dsa.topk_overlap(torch.zeros(3, 2, 4, dtype=torch.int32), 10)
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out must have shape"):
+        dsa.quantize_fp8_rows(x, out=torch.zeros(4, 32, dtype=torch.float8_e4m3fn))
+    with pytest.raises(ValueError, match="one entry per row"):
+        dsa.quantize_fp8_rows(x, scale=torch.zeros(5))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        dsa.quantize_fp8_rows(x)
+
