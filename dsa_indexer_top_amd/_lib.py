@@ -14,6 +14,8 @@ DSA_ERR_BAD_PATTERN = 3
 DSA_ERR_WORKSPACE = 4
 DSA_ERR_HIP = 5
 
+DSA_STATIC_SCRATCH_BYTES = 64 << 20   # include/dsa.h
+
 DSA_BF16 = 0
 DSA_FP8_E4M3FN = 1
 
@@ -25,6 +27,7 @@ EXPORTS = (
     "dsa_stack_workspace_size",
     "dsa_resolve_pattern",
     "dsa_indexer_scores_topk",
+    "dsa_indexer_scores_topk_static",
     "dsa_sparse_attn",
     "dsa_layer_stack_run",
     "dsa_chunked_stack_workspace_size",
@@ -116,6 +119,8 @@ def load() -> ctypes.CDLL:
     lib.dsa_resolve_pattern.argtypes = [c_int32, c_char_p, c_int32, ctypes.c_char_p]
     lib.dsa_indexer_scores_topk.restype = c_int32
     lib.dsa_indexer_scores_topk.argtypes = [POINTER(IndexerArgs), c_void_p]
+    lib.dsa_indexer_scores_topk_static.restype = c_int32
+    lib.dsa_indexer_scores_topk_static.argtypes = [POINTER(IndexerArgs), c_void_p]
     lib.dsa_sparse_attn.restype = c_int32
     lib.dsa_sparse_attn.argtypes = [POINTER(AttnArgs), c_void_p]
     lib.dsa_layer_stack_run.restype = c_int32

@@ -168,8 +168,12 @@ def indexer_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk:
                         out_idx: Optional[torch.Tensor] = None,
                         out_scores=False, debug_full_scores=False,
                         workspace: Optional[torch.Tensor] = None,
-                        stream=None, phase_events=None) -> IndexerResult:
+                        stream=None, phase_events=None, static_scratch: bool = False) -> IndexerResult:
     """Lightning-indexer scores + exact per-query top-k (dsa_indexer_scores_topk).
+
+    static_scratch=True calls dsa_indexer_scores_topk_static instead: no
+    workspace is allocated or passed (the library's static device scratch is
+    used; pass out_idx and the other outputs to allocate nothing at all).
 
     q [B, n_q, H, D], k [B, n_k, D] (bf16 or float8_e4m3fn), w [B, n_q, H] fp32,
     fp8: q_scale [B, n_q], k_scale [B, n_k] fp32. out_scores / debug_full_scores
@@ -209,9 +213,14 @@ def indexer_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk:
     elif isinstance(debug_full_scores, torch.Tensor):
         full = debug_full_scores
     a = indexer_args(B, n_q, n_k, pos_offset, H, D, topk, code)
-    nbytes = ctypes.c_size_t(0)
-    _check(L.load().dsa_indexer_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
-    ws = _workspace(int(nbytes.value), dev, workspace)
+    if static_scratch:
+        if workspace is not None:
+            raise ValueError("static_scratch takes no workspace")
+        ws = None
+    else:
+        nbytes = ctypes.c_size_t(0)
+        _check(L.load().dsa_indexer_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+        ws = _workspace(int(nbytes.value), dev, workspace)
     a.q, a.k, a.w = _ptr(q), _ptr(k), _ptr(w)
     a.q_scale, a.k_scale = _ptr(q_scale), _ptr(k_scale)
     a.out_idx, a.out_scores, a.debug_full_scores = _ptr(out_idx), _ptr(sc), _ptr(full)
@@ -219,7 +228,8 @@ def indexer_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk:
     a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     keep = _event_array(phase_events, 3)
     a.phase_events = None if keep is None else ctypes.cast(keep, ctypes.c_void_p)
-    _check(L.load().dsa_indexer_scores_topk(ctypes.byref(a), _stream(stream)))
+    fn = L.load().dsa_indexer_scores_topk_static if static_scratch else L.load().dsa_indexer_scores_topk
+    _check(fn(ctypes.byref(a), _stream(stream)))
     return IndexerResult(out_idx, sc, full)
 
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 #include <string>
 
@@ -362,6 +363,70 @@ dsa_status dsa_indexer_scores_topk(const dsa_indexer_args* a, void* stream) {
   if (st != DSA_OK) return st;
   dsa::IndexerParams p = make_indexer_params(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx,
                                              a->out_scores, a->debug_full_scores, a->workspace);
+  p.ev = a->phase_events;
+  st = run_indexer(p, (hipStream_t)stream);
+  return st == DSA_OK ? ok() : st;
+}
+
+}  // extern "C"
+
+// ---- the no-allocation variant of dsa_indexer_scores_topk
+//
+// The scratch space lives in this file-scope device array instead of a caller
+// workspace. Every GPU the library runs on holds its own copy until the
+// process ends. Host code never passes the array's name to a kernel (in host
+// code it is only a stand-in for the symbol): the device address of each
+// GPU's copy is looked up once per device with hipGetSymbolAddress and kept in
+// g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[DSA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's scratch array, looked up on
+// the device's first call.
+dsa_status scratch_for_current_device(const char* what, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", what, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", what, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_indexer_scores_topk_static(const dsa_indexer_args* a, void* stream) {
+  const char* what = "indexer_scores_topk_static";
+  dsa_status st = check_indexer_shape(a, what);
+  if (st != DSA_OK) return st;
+  st = check_indexer_ptrs(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx, what);
+  if (st != DSA_OK) return st;
+  if ((a->out_scores && !aligned(a->out_scores, 4)) || (a->debug_full_scores && !aligned(a->debug_full_scores, 4)))
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: misaligned out_scores/debug_full_scores", what);
+  if (a->workspace || a->workspace_bytes)
+    return fail(DSA_ERR_INVALID_ARGUMENT, "%s: takes no workspace (workspace must be NULL, workspace_bytes 0)", what);
+  const size_t need = dsa::indexer_workspace_bytes(a->B, a->n_q, a->n_k, a->topk);
+  if (need > (size_t)DSA_STATIC_SCRATCH_BYTES)
+    return fail(DSA_ERR_WORKSPACE, "%s: this shape needs %zu bytes of scratch, the static scratch holds %zu",
+                what, need, (size_t)DSA_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_for_current_device(what, &ws);
+  if (st != DSA_OK) return st;
+  dsa::IndexerParams p = make_indexer_params(a, a->q, a->k, a->w, a->q_scale, a->k_scale, a->out_idx,
+                                             a->out_scores, a->debug_full_scores, ws);
   p.ev = a->phase_events;
   st = run_indexer(p, (hipStream_t)stream);
   return st == DSA_OK ? ok() : st;

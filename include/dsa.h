@@ -228,6 +228,25 @@ dsa_status dsa_resolve_pattern(int32_t n_layers, const char *pattern, int32_t in
  * matrix is never stored (except in debug_full_scores test mode). */
 dsa_status dsa_indexer_scores_topk(const dsa_indexer_args *args, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as dsa_indexer_scores_topk, with the library's own scratch in
+ * place of a workspace. args->workspace must be NULL and workspace_bytes 0.
+ * The scratch is a static device array of DSA_STATIC_SCRATCH_BYTES (64 MiB)
+ * that each GPU holds from the first call on it until the process ends; a
+ * shape whose dsa_indexer_workspace_size exceeds it returns DSA_ERR_WORKSPACE
+ * before anything is enqueued (e.g. decode of B = 32 requests over 200K-token
+ * contexts at topk = 2048 needs about 28 MB; prefill needs about 64 KB per
+ * query row at topk = 2048). The call allocates nothing, on the device or
+ * through any library. Every call on one GPU shares that GPU's scratch and
+ * the scratch keeps the last call's contents (the kernels initialise what
+ * they read): calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. The first call on a
+ * device looks up the array's device address (hipGetSymbolAddress); a
+ * failure there is DSA_ERR_HIP. */
+#define DSA_STATIC_SCRATCH_BYTES (64u << 20)
+dsa_status dsa_indexer_scores_topk_static(const dsa_indexer_args *args, void *stream);
+
 /* Softmax attention of every query head over the key/value rows listed in idx. */
 dsa_status dsa_sparse_attn(const dsa_attn_args *args, void *stream);
 

@@ -429,3 +429,21 @@ def test_binding_other_argument_checks():
     with pytest.raises(ValueError, match="must be a GPU tensor"):
         dsa.quantize_fp8_rows(x)
 
+
+def test_static_scratch_entry_validation(lib):
+    """The no-allocation entry point validates like dsa_indexer_scores_topk,
+    refuses a workspace, and rejects shapes beyond its static scratch before
+    any HIP call."""
+    f = lib.dsa_indexer_scores_topk_static
+    a = _idx_args()
+    a.q = None
+    assert f(ctypes.byref(a), None) == L.DSA_ERR_INVALID_ARGUMENT
+    a = _idx_args()
+    a.workspace, a.workspace_bytes = FAKE, 1 << 20
+    assert f(ctypes.byref(a), None) == L.DSA_ERR_INVALID_ARGUMENT
+    a = _idx_args(n_q=4096, n_k=4096, topk=2048)
+    assert dsa.indexer_workspace_size(1, 4096, 4096, 64, 128, 2048) > L.DSA_STATIC_SCRATCH_BYTES
+    assert f(ctypes.byref(a), None) == L.DSA_ERR_WORKSPACE
+    assert b"static scratch" in lib.dsa_last_error()
+    # decode of 32 requests over 200K tokens fits
+    assert dsa.indexer_workspace_size(32, 1, 200000, 64, 128, 2048) <= L.DSA_STATIC_SCRATCH_BYTES
