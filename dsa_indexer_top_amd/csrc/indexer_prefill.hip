@@ -103,32 +103,55 @@ __device__ int coop_excl_scan(int v, ShrinkLds& sh, int* total) {
   return before + (int)incl - v;
 }
 
+// A shrink reads the list in rounds of 8 entries per thread, each thread
+// taking 8 consecutive entries with two 16-byte loads: a round covers 2048
+// entries (four rounds for C = 8192), so a pass over the list costs four
+// memory round trips. (16 entries per thread would halve that again but push
+// the kernel's registers past 256.)
+constexpr int kShrinkPerThread = 8;
+
+// Loads the list entries of this thread in the round starting at `base`
+// (entries at or past cnt read as 0). cnt <= C and C is a multiple of 64, so a
+// 16-byte quad that starts below cnt lies inside the row's list.
+// The loads are unconditional, clamped into the row's list (cap = C entries);
+// the masking is arithmetic, so no per-entry condition mask is kept live.
+template <typename T>
+__device__ __forceinline__ void load_round(const T* __restrict__ src, int base, int cnt, int cap,
+                                           T (&v)[kShrinkPerThread]) {
+  const int i0 = base + (int)threadIdx.x * kShrinkPerThread;
+#pragma unroll
+  for (int q = 0; q < kShrinkPerThread / 4; ++q) {
+    const i32x4 x = *(const i32x4*)(src + min(i0 + 4 * q, cap - 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int m = (i0 + 4 * q + e - cnt) >> 31;  // all ones below cnt
+      asm volatile("" : "+v"(m));             // kept as a lane mask, not a condition
+      v[4 * q + e] = (T)(x[e] & m);
+    }
+  }
+}
+
 // One radix-select step over an 8-bit digit of the listed keys whose higher
 // bits match `prefix` under `pmask`: the whole workgroup builds the 256-bin
-// histogram (4 keys in flight per thread), wave 0 finds the digit holding the
-// rem-th largest such key. Returns the digit; *above / *in_d = matching keys
-// with a larger digit / with this digit.
+// histogram, wave 0 finds the digit holding the rem-th largest such key.
+// Returns the digit; *above / *in_d = matching keys with a larger digit /
+// with this digit. Entries past cnt read as key 0, which lies below every
+// score's key and so below the selected digit.
 template <int W>
-__device__ int coop_digit_step(const uint32_t* __restrict__ keys, int cnt, uint32_t prefix, uint32_t pmask,
+__device__ int coop_digit_step(const uint32_t* __restrict__ keys, int cnt, int cap, uint32_t prefix, uint32_t pmask,
                                int shift, uint32_t rem, ShrinkLds& sh, uint32_t* above, uint32_t* in_d) {
   constexpr int NT = W * kWave;
   for (int i = threadIdx.x; i < 256 * kShrinkHistCopies; i += NT) sh.hist[i] = 0u;
   __syncthreads();
   const uint32_t copy = threadIdx.x % kShrinkHistCopies;
-  constexpr int DB = 4;  // keys in flight per thread
 #pragma unroll 1
-  for (int base = 0; base < cnt; base += DB * NT) {
-    uint32_t u[DB];
+  for (int base = 0; base < cnt; base += kShrinkPerThread * NT) {
+    uint32_t u[kShrinkPerThread];
+    load_round(keys, base, cnt, cap, u);
 #pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      const int i = base + j * NT + (int)threadIdx.x;
-      u[j] = i < cnt ? keys[i] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      const int i = base + j * NT + (int)threadIdx.x;
-      if (i < cnt && (u[j] & pmask) == prefix)
-        atomicAdd(&sh.hist[((u[j] >> shift) & 255u) * kShrinkHistCopies + copy], 1u);
+    for (int j = 0; j < kShrinkPerThread; ++j) {
+      if ((u[j] & pmask) == prefix) atomicAdd(&sh.hist[((u[j] >> shift) & 255u) * kShrinkHistCopies + copy], 1u);
+      __builtin_amdgcn_sched_barrier(0);  // one entry's condition at a time
     }
   }
   __syncthreads();
@@ -175,48 +198,50 @@ __device__ int coop_digit_step(const uint32_t* __restrict__ keys, int cnt, uint3
 
 // Ordered in-place compaction by the workgroup: keeps every key > theta and
 // the first `ties_left` keys == theta, in list order; returns the new length.
-// Each thread owns CE consecutive entries of a round; all of a round is read
+// Each thread owns consecutive entries of a round; all of a round is read
 // before any of it is written (the scans hold barriers), and a round only
-// writes below its own end.
+// writes below its own end. Entries past cnt read as key 0 and are never
+// kept (theta is above 0: it is a kept key's prefix, and every score's key
+// is at least 2^23).
 template <int W>
-__device__ int coop_compact(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, int cnt, uint32_t theta,
+__device__ int coop_compact(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, int cnt, int cap, uint32_t theta,
                             int ties_left, ShrinkLds& sh) {
   constexpr int NT = W * kWave;
-  constexpr int CE = 4;
+  constexpr int E = kShrinkPerThread;
   int out = 0, ties = 0;
 #pragma unroll 1
-  for (int base = 0; base < cnt; base += CE * NT) {
-    const int i0 = base + CE * (int)threadIdx.x;
-    uint32_t u[CE];
-    int32_t s[CE];
+  for (int base = 0; base < cnt; base += E * NT) {
+    uint32_t u[E];
+    int32_t s[E];
+    load_round(keys, base, cnt, cap, u);
+    load_round(idxs, base, cnt, cap, s);
     int nt = 0;
 #pragma unroll
-    for (int j = 0; j < CE; ++j) {
-      const bool in = i0 + j < cnt;
-      u[j] = in ? keys[i0 + j] : 0u;
-      s[j] = in ? idxs[i0 + j] : 0;
-      nt += (in && u[j] == theta) ? 1 : 0;
+    for (int j = 0; j < E; ++j) {
+      nt += u[j] == theta ? 1 : 0;
+      __builtin_amdgcn_sched_barrier(0);
     }
     int tie_total;
     int tr = ties + coop_excl_scan<W>(nt, sh, &tie_total);
-    int nk = 0;
     uint32_t keep = 0u;
 #pragma unroll
-    for (int j = 0; j < CE; ++j) {
-      const bool in = i0 + j < cnt;
-      const bool kj = in && (u[j] > theta || (u[j] == theta && tr++ < ties_left));
+    for (int j = 0; j < E; ++j) {
+      const bool eq = u[j] == theta;
+      const bool kj = u[j] > theta || (eq && tr < ties_left);
+      tr += eq ? 1 : 0;
       keep |= kj ? (1u << j) : 0u;
-      nk += kj ? 1 : 0;
+      __builtin_amdgcn_sched_barrier(0);
     }
     int keep_total;
-    int pos = out + coop_excl_scan<W>(nk, sh, &keep_total);
+    int pos = out + coop_excl_scan<W>(__popc(keep), sh, &keep_total);
 #pragma unroll
-    for (int j = 0; j < CE; ++j) {
+    for (int j = 0; j < E; ++j) {
       if ((keep >> j) & 1u) {
         keys[pos] = u[j];
         idxs[pos] = s[j];
         ++pos;
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     out += keep_total;
     ties += tie_total;
@@ -237,8 +262,8 @@ __device__ int coop_compact(uint32_t* __restrict__ keys, int32_t* __restrict__ i
 // k-th key theta and the list keeps exactly k entries: those > theta and the
 // lowest-index ties (the list is in index order).
 template <int W>
-__device__ __forceinline__ void coop_shrink(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, int cnt, int k,
-                                            int keep_max, ShrinkLds& sh, uint32_t* theta_out, int* cnt_out) {
+__device__ __forceinline__ void coop_shrink(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, int cnt, int cap,
+                                            int k, int keep_max, ShrinkLds& sh, uint32_t* theta_out, int* cnt_out) {
   uint32_t prefix = 0u, pmask = 0u;
   uint32_t rem = (uint32_t)k;
   int ties_left = 1 << 30;
@@ -246,14 +271,14 @@ __device__ __forceinline__ void coop_shrink(uint32_t* __restrict__ keys, int32_t
   for (int st = 0; st < 4; ++st) {
     uint32_t above, in_d;
     const int shift = 24 - 8 * st;
-    const int d = coop_digit_step<W>(keys, cnt, prefix, pmask, shift, rem, sh, &above, &in_d);
+    const int d = coop_digit_step<W>(keys, cnt, cap, prefix, pmask, shift, rem, sh, &above, &in_d);
     rem -= above;
     prefix |= (uint32_t)d << shift;
     pmask |= 0xFFu << shift;
     if (st == 1 && (int)((uint32_t)k - rem + in_d) <= keep_max) break;  // keys with prefix >= P fit
     if (st == 3) ties_left = (int)rem;
   }
-  const int n = coop_compact<W>(keys, idxs, cnt, prefix, ties_left, sh);
+  const int n = coop_compact<W>(keys, idxs, cnt, cap, prefix, ties_left, sh);
   if (threadIdx.x == 0) {
     *theta_out = prefix;
     *cnt_out = n;
@@ -387,6 +412,25 @@ void indexer_prefill_kernel(IndexerParams p) {
     dma_sub(2 * tile, lds_k[buf]);
     dma_sub(2 * tile + 1, lds_k[buf] + T::kBytes);
   };
+  // The loads of a whole tile (both sub-tiles full), spread over the KS
+  // chunks of a half tile: load i of the 2 * CPT goes with chunk
+  // i * KS / (2 * CPT), so a wave never issues its tile share in one burst
+  // (the workgroup's waves would queue on the vector memory path together,
+  // right after the barrier, and stall their next MFMAs).
+  auto dma_full_part = [&](int tile, int buf, int ks) {
+#pragma unroll
+    for (int i = 0; i < 2 * CPT; ++i) {
+      if (min(KS - 1, i * KS / (2 * CPT)) != ks) continue;
+      const int sub = i / CPT, c = i % CPT;
+      const int q0 = c * NT + wave * kWave;  // first 16-byte LDS slot of this wave's load (uniform)
+      if (q0 < T::kSlots) {
+        const unsigned char* src = kbase + (size_t)(2 * tile + sub) * kTileKeys * T::kRowBytes;
+        uint32_t o = (voff[c / 2] >> (16 * (c & 1))) & 0xFFFFu;
+        asm volatile("" : "+v"(o));
+        lds_load16(src + o, lds_k[buf] + sub * T::kBytes + 16 * q0);
+      }
+    }
+  };
 
   uint32_t theta = 0u;
   int cnt = 0;
@@ -473,7 +517,7 @@ void indexer_prefill_kernel(IndexerParams p) {
         // otherwise sink it below every fence)
         asm volatile("" : "+v"(s0), "+v"(s1));
       }
-      if (ks == SIDE_KS) side();
+      side(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
     return s0 + s1;
@@ -557,7 +601,7 @@ void indexer_prefill_kernel(IndexerParams p) {
     for (int w = 0; w < kPrefillWaves; ++w) {
       if (!((flags >> w) & 1u) || shl.cnt[w] <= p.C - kListMargin) continue;
       const size_t rw = (size_t)b * p.n_q + qb * kPrefillWaves + w;
-      coop_shrink<kPrefillWaves>(p.cand_key + rw * p.C, p.cand_idx + rw * p.C, shl.cnt[w], p.topk, p.C - kListMargin, shl,
+      coop_shrink<kPrefillWaves>(p.cand_key + rw * p.C, p.cand_idx + rw * p.C, shl.cnt[w], p.C, p.topk, p.C - kListMargin, shl,
                   &shl.theta[w], &shl.cnt[w]);
       __syncthreads();
     }
@@ -570,7 +614,9 @@ void indexer_prefill_kernel(IndexerParams p) {
     if (threadIdx.x == 0) shl.flags[par] = 0u;
     __syncthreads();
   };
-  auto no_side = [&]() {};
+  auto no_side = [&](int) {};
+  // callbacks run inside a chunk of a half tile: `f` once, at chunk SIDE_KS
+  auto at_side = [&](auto&& f) { return [&f](int ks) { if (ks == SIDE_KS) f(); }; };
 
   f32x16 accA[MB], accB[MB];
   if (n_tiles > 0) dma_tile(0, 0);
@@ -615,7 +661,8 @@ void indexer_prefill_kernel(IndexerParams p) {
     const int par = tile % 3, prev = (tile + 2) % 3;
     float q0 = 0.0f, q1 = 0.0f, q2 = 0.0f, q3 = 0.0f;
     if (mine)
-      q0 = half_step(TrueT{}, TrueT{}, TrueT{}, TrueT{}, lds_k[cur], 1, lds_k[cur], 2, accB, accA, filter_compute_a);
+      q0 = half_step(TrueT{}, TrueT{}, TrueT{}, TrueT{}, lds_k[cur], 1, lds_k[cur], 2, accB, accA,
+                     at_side(filter_compute_a));
     else filter_compute_a();
     if (mine) {
       q1 = half_step(TrueT{}, TrueT{}, TrueT{}, TrueT{}, lds_k[cur], 2, lds_k[cur], 3, accA, accB, no_side);
@@ -625,7 +672,7 @@ void indexer_prefill_kernel(IndexerParams p) {
       pend_base = base;
       pend_end = kend;
       q2 = half_step(TrueT{}, TrueT{}, TrueT{}, FalseT{}, lds_k[cur], 3, lds_k[cur], 0, accB, accA,
-                     filter_compute);
+                     at_side(filter_compute));
     } else {
       filter_compute();
     }
@@ -638,14 +685,25 @@ void indexer_prefill_kernel(IndexerParams p) {
     // next written two iterations later, after the next barrier).
     uint32_t flags_v = 0u;
     auto read_flags = [&]() { flags_v = shl.flags[prev]; };
-    if (tile + 2 < n_tiles) dma_tile(tile + 2, cur);
+    // Tile+2 goes into the buffer this tile leaves (every wave has read it:
+    // the barrier above). A whole tile's loads are spread over this half
+    // tile's chunks; a ragged last tile, or a wave without a half tile to
+    // compute, issues them at once.
+    const int dtile = tile + 2;
+    const bool do_dma = dtile < n_tiles;
+    const bool spread = do_dma && mine && (2 * dtile + 2) * kTileKeys <= p.n_k;
+    if (do_dma && !spread) dma_tile(dtile, cur);
+    auto q3_side = [&](int ks) {
+      if (ks == SIDE_KS) read_flags();
+      if (spread) dma_full_part(dtile, cur, ks);
+    };
     if (mine) {
       if (mine_next)
         q3 = half_step(TrueT{}, TrueT{}, FalseT{}, TrueT{}, lds_k[cur ^ 1], 0, lds_k[cur ^ 1], 1, accA, accB,
-                       read_flags);
+                       q3_side);
       else
         q3 = half_step(TrueT{}, FalseT{}, FalseT{}, FalseT{}, lds_k[cur], 0, lds_k[cur], 0, accA, accB,
-                       read_flags);
+                       q3_side);
       pend_p0 = q2;
       pend_p1 = q3;
       pend_ksc = ksc1;
