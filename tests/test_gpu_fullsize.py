@@ -302,7 +302,11 @@ def test_c4_decode_stack_200k(dsa, B):
         src = res[max(f for f in fl if f <= l)].idx
         o, _ = dsa.sparse_attn(layers[l]["q"], layers[l]["k"], layers[l]["v"], src)
         torch.cuda.synchronize()
-        assert torch.equal(o, st.outs[l]), f"layer {l} ({pat[l]}) did not attend over its F layer's indices"
+        if not torch.equal(o, st.outs[l]):
+            diff = (o.float() - st.outs[l].float()).abs().amax(dim=(1, 2, 3))
+            bad = torch.nonzero(diff).flatten().tolist()
+            raise AssertionError(f"layer {l} ({pat[l]}) did not attend over its F layer's indices: requests {bad} "
+                                 f"differ, max abs {diff.max().item()}")
     for f in fl:
         _check_decode_layer(dsa, inps[f], res[f], topk, T, B, f"C4 B={B} layer {f}")
     # attention against the oracle: the F layer and the S layer after it, a few requests
