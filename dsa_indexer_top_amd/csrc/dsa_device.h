@@ -53,6 +53,21 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Kernel arguments sit in memory the host has just written, so each batch of
+// argument loads that waits for an earlier one (a load behind a branch on
+// another argument, the grid size read once the block's range is needed)
+// costs one more trip to HBM, about a microsecond, before a short kernel
+// issues its first data load. The short decode kernels name every argument
+// they use at entry, which puts all of those loads in one batch.
+__device__ __forceinline__ void arg_now(const void* v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ void arg_now(int v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ void arg_now(unsigned v) { asm volatile("" ::"s"(v)); }
+__device__ __forceinline__ void arg_now(float v) { asm volatile("" ::"s"(v)); }
+template <typename... T>
+__device__ __forceinline__ void args_now(const T&... v) {
+  (arg_now(v), ...);
+}
 __device__ __forceinline__ uint32_t uniform_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }

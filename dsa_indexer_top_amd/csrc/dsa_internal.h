@@ -37,7 +37,7 @@ __host__ __device__ inline size_t decode_key_stride(int n_k) { return ((size_t)n
 constexpr int kDecodeWaveKeys = 32;          // keys per wave step of the score kernel
 constexpr int kDecodeBlockKeys = 4 * kDecodeWaveKeys;
 constexpr int kDecodeCollectKeys = 4096;     // keys per block of the collect kernel
-constexpr int kDecodeTargetBlocks = 512;     // score blocks per decode call (two per CU)
+constexpr int kDecodeTargetBlocks = 256;     // score blocks per decode call (one per CU)
 
 // Paged, ragged decode: token s of request b is row
 // block_table[b * max_pages + s / page_size] * page_size + s % page_size of the

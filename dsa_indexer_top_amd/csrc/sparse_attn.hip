@@ -70,6 +70,8 @@ __device__ __forceinline__ void sparse_attn_body(const AttnParams& p) {
   using S = AttnShape<D>;
   static_assert((S::PSTRIDE / 4) % 64 == 16, "lane groups of a read must not share banks");
   __shared__ __attribute__((aligned(16))) unsigned char lds_v[WAVES][16 * S::PSTRIDE];
+  args_now(p.nsplit, p.B, p.n_q, p.n_k, p.pos_offset, p.topk, p.H, p.scale, p.q, p.k, p.v, p.idx, p.part, p.out, p.lse,
+           p.kv.seq_lens, p.kv.block_table);
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   __builtin_assume(wave >= 0 && wave < WAVES);
@@ -373,6 +375,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
 template <int D, int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   constexpr int DPL = D / kWave;  // output dims per lane
+  args_now(p.H, p.nsplit, p.part, p.out, p.lse);
   const int lane = lane_id();
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int row = blockIdx.y;

@@ -489,6 +489,8 @@ __global__ __launch_bounds__(kFinNTPrefill) __attribute__((amdgpu_waves_per_eu(4
 __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeParams p) {
   static_assert(kFinNTDecode == kSortWaves * kWave && kSortN >= kMaxTopk, "sort layout");
   static_assert(kMaxC >= 2 * kSortN + 256 * kSortWaves, "sort scratch must fit in skey");
+  args_now((int)blockDim.x, p.kv.seq_lens, p.pos_offset, p.n_k, p.topk, p.C, p.cand_key, p.cand_idx, p.cand_cnt,
+           p.cnt_stride, p.dec_hist, p.out_idx, p.out_scores, p.full_keys);
   // one LDS buffer: the bucket path's order words and bucket counts, or the
   // sort path's candidate keys (skey) and winners (wkey, widx)
   constexpr int kBits = 12;  // few workgroups: the finest buckets that fit
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(256) void decode_prepare_kernel(IndexerParams p, si
   __syncthreads();
   const unsigned long long U = sh_units;
   // aim at target - B blocks so that the rounding up per request still leaves
-  // at most target blocks: one even round of two blocks per CU, no tail
+  // at most target blocks: one even round of a block per CU, no tail
   const unsigned long long aim = (unsigned long long)max(kDecodeTargetBlocks - p.B, kDecodeTargetBlocks / 2);
   const long long per = U == 0ull ? 1ll : (long long)((U + aim - 1) / aim);
   const long long span = per * kDecodeBlockKeys;  // keys per planned block
@@ -711,6 +713,9 @@ struct DecodeTile {
 template <int D, int MB, bool FP8, bool DUMP>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
   using T = DecodeTile<D, FP8>;
+  const int grid_x = gridDim.x;
+  args_now(grid_x, p.q, p.w, p.q_scale, p.k, p.k_scale, p.dec_keys, p.dec_hist, p.dec_work, p.dump, p.kv.seq_lens,
+           p.kv.block_table, p.n_q, p.n_k, p.H, p.pos_offset);
   constexpr int KS = FP8 ? D / 64 : D / 16;
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type Frag;
   __shared__ uint32_t hist[kDecodeHistBins];
@@ -729,48 +734,13 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     // one length for all: gridDim.x blocks split each request's keys evenly
     b = blockIdx.y;
     const int kend = decode_len(p.kv, b, p.pos_offset, p.n_k);
-    const int per = ((kend + (int)gridDim.x - 1) / (int)gridDim.x + kDecodeBlockKeys - 1) / kDecodeBlockKeys *
+    const int per = ((kend + grid_x - 1) / grid_x + kDecodeBlockKeys - 1) / kDecodeBlockKeys *
                     kDecodeBlockKeys;
     k0 = blockIdx.x * per;
     k1 = min(k0 + per, kend);
   }
   const int i32 = lane & 31, g = lane >> 5;
   const size_t row = (size_t)b * p.n_q;  // n_q == 1
-
-  for (int i = threadIdx.x; i < kDecodeHistBins; i += blockDim.x) hist[i] = 0u;
-
-  Frag qa[MB][KS];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int head = 32 * mb + i32;
-    const bool ok = head < p.H;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (FP8) {
-        i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (ok) {
-          const unsigned char* src = (const unsigned char*)p.q + (row * p.H + head) * D + g * (D / 2) + 32 * ks;
-          const i32x4 lo = *(const i32x4*)src, hi = *(const i32x4*)(src + 16);
-          v = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        qa[mb][ks] = v;
-      } else {
-        bf16x8 v = {};
-        if (ok) v = *(const bf16x8*)((const __bf16*)p.q + (row * p.H + head) * D + g * (D / 2) + 8 * ks);
-        qa[mb][ks] = v;
-      }
-    }
-  }
-  float wr[MB][16];
-  const float qs = FP8 ? p.q_scale[row] : 1.0f;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int head = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-      wr[mb][r] = head < p.H ? p.w[row * p.H + head] * qs : 0.0f;
-    }
-  __syncthreads();  // histogram cleared
 
   const bool paged = p.kv.block_table != nullptr;
   const unsigned char* kbase = (const unsigned char*)p.k + (paged ? 0 : (size_t)b * p.n_k * T::RB);
@@ -812,6 +782,67 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     }
     if constexpr (FP8) ksc = kscale[r0 + min(i32, last)];
   };
+  // the first two steps' rows are requested before anything else, so that
+  // the query and weight loads and the histogram clear below overlap them
+  i32x4 buf0[T::NI], buf1[T::NI];
+  float ksc0 = 0.0f, ksc1 = 0.0f;
+  int base = k0 + kDecodeWaveKeys * wave;
+  if (base < k1) load_step(buf0, ksc0, base);
+  if (base + kDecodeBlockKeys < k1) load_step(buf1, ksc1, base + kDecodeBlockKeys);
+
+  static_assert(kDecodeHistBins % (4 * 256) == 0, "histogram clear");
+#pragma unroll
+  for (int i = 0; i < kDecodeHistBins / (4 * 256); ++i) ((uint4*)hist)[threadIdx.x + 256 * i] = make_uint4(0u, 0u, 0u, 0u);
+
+  Frag qa[MB][KS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int head = 32 * mb + i32;
+    const bool ok = head < p.H;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (FP8) {
+        i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (ok) {
+          const unsigned char* src = (const unsigned char*)p.q + (row * p.H + head) * D + g * (D / 2) + 32 * ks;
+          const i32x4 lo = *(const i32x4*)src, hi = *(const i32x4*)(src + 16);
+          v = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        qa[mb][ks] = v;
+      } else {
+        bf16x8 v = {};
+        if (ok) v = *(const bf16x8*)((const __bf16*)p.q + (row * p.H + head) * D + g * (D / 2) + 8 * ks);
+        qa[mb][ks] = v;
+      }
+    }
+  }
+  // lane weights: heads 32*mb + 8*(r/4) + 4g + r%4, four consecutive heads
+  // per 16-byte load when every row of w starts 16-byte aligned (H % 4 == 0)
+  float wr[MB][16];
+  const float qs = FP8 ? p.q_scale[row] : 1.0f;
+  if ((p.H & 3) == 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int head = 32 * mb + 8 * j + 4 * g;
+        const float4 x = head < p.H ? *(const float4*)(p.w + row * p.H + head) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        wr[mb][4 * j] = x.x * qs;
+        wr[mb][4 * j + 1] = x.y * qs;
+        wr[mb][4 * j + 2] = x.z * qs;
+        wr[mb][4 * j + 3] = x.w * qs;
+      }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int head = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+        wr[mb][r] = head < p.H ? p.w[row * p.H + head] * qs : 0.0f;
+      }
+  }
+  __syncthreads();  // histogram cleared
+
   // one step: rows to LDS, refill the buffer with the step two ahead, MFMAs
   // on fragments read from LDS, epilogue
   auto step = [&](i32x4 (&buf)[T::NI], float& ksc, int base) {
@@ -863,11 +894,6 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     }
   };
 
-  i32x4 buf0[T::NI], buf1[T::NI];
-  float ksc0 = 0.0f, ksc1 = 0.0f;
-  int base = k0 + kDecodeWaveKeys * wave;
-  if (base < k1) load_step(buf0, ksc0, base);
-  if (base + kDecodeBlockKeys < k1) load_step(buf1, ksc1, base + kDecodeBlockKeys);
   for (; base < k1; base += 2 * kDecodeBlockKeys) {
     step(buf0, ksc0, base);
     if (base + kDecodeBlockKeys >= k1) break;
@@ -875,7 +901,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
   }
   __syncthreads();
   uint32_t* gh = p.dec_hist + (size_t)b * kDecodeHistStride;
-  for (int i = threadIdx.x; i < kDecodeHistBins; i += blockDim.x) {
+  for (int i = threadIdx.x; i < kDecodeHistBins; i += 256) {
     const uint32_t c = hist[i];
     if (c) atomicAdd(&gh[i], c);
   }
@@ -911,6 +937,8 @@ __device__ int wave_threshold_bin(const uint32_t* __restrict__ gh, int k_eff) {
 // finalize kernel then takes the exact full-row select). One atomic per block
 // reserves the block's slots.
 __global__ __launch_bounds__(256) void decode_collect_kernel(IndexerParams p) {
+  args_now(p.kv.seq_lens, p.pos_offset, p.n_k, p.topk, p.dec_hist, p.dec_keys, p.cand_cnt, p.cand_key, p.cand_idx, p.C,
+           p.cnt_stride);
   __shared__ int scratch[17];
   __shared__ int sh_base;
   const int b = blockIdx.y;
