@@ -212,7 +212,7 @@ size_t indexer_workspace_bytes(int B, int n_q, int n_k, int topk) {
   if (n_q == 1) {
     sz += (size_t)B * decode_key_stride(n_k) * 4;                    // decode keys
     sz += round_up(((size_t)B + kDecodeTargetBlocks) * 3 * 4, 256);  // ragged-decode block plan
-    sz += (size_t)B * kDecodeHistStride * 4;  // decode histograms and counters
+    sz += (size_t)B * kDecodeHistRow * 4;  // decode histograms and counters
   } else {
     sz += round_up(rows * 4, 256);  // cand_cnt
   }
@@ -234,7 +234,7 @@ void indexer_bind_workspace(IndexerParams& p, void* ws) {
     c += round_up(((size_t)p.B + kDecodeTargetBlocks) * 3 * 4, 256);
     p.dec_hist = (uint32_t*)c;
     p.cand_cnt = (int32_t*)(p.dec_hist + kDecodeCntOffset);
-    p.cnt_stride = kDecodeHistStride;
+    p.cnt_stride = kDecodeHistRow;
   } else {
     p.cand_cnt = (int32_t*)c;
     p.cnt_stride = 1;

@@ -31,6 +31,12 @@ constexpr int kDecodeCoarseBins = 64;  // sums of 64 consecutive bins, stored af
 // apart, so the collect blocks' atomics on them do not queue on one line).
 constexpr int kDecodeCntOffset = kDecodeHistBins + kDecodeCoarseBins;
 constexpr int kDecodeHistStride = kDecodeCntOffset + 64;
+// A request's histogram is kept in kDecodeHistCopies copies (score block j
+// adds to copy j mod kDecodeHistCopies), so the blocks' atomics on the few
+// bins that hold most keys queue on eight addresses instead of one; readers
+// sum the copies. The request's counter is the one in copy 0.
+constexpr int kDecodeHistCopies = 8;
+constexpr int kDecodeHistRow = kDecodeHistCopies * kDecodeHistStride;
 // Row stride of the decode score keys: n_k rounded up to 64 keys (256 B), so
 // every row starts aligned and 16-key vector reads stay inside it.
 __host__ __device__ inline size_t decode_key_stride(int n_k) { return ((size_t)n_k + 63) / 64 * 64; }
@@ -78,10 +84,10 @@ struct IndexerParams {
   uint32_t* cand_key;   // [rows, C]
   int32_t* cand_idx;    // [rows, C]
   int32_t* cand_cnt;    // [rows], row r at cand_cnt[r * cnt_stride]
-  int cnt_stride;       // 1 (prefill) or kDecodeHistStride (decode: inside the histogram rows)
+  int cnt_stride;       // 1 (prefill) or kDecodeHistRow (decode: inside the histogram rows)
   int C;
   uint32_t* dec_keys;   // decode: [B, dec_stride] score keys
-  uint32_t* dec_hist;   // decode: [B, kDecodeHistStride] (fine bins, coarse bins, counter)
+  uint32_t* dec_hist;   // decode: [B, kDecodeHistCopies, kDecodeHistStride] (fine bins, coarse bins, counter)
   int32_t* dec_work;    // decode: [B + kDecodeTargetBlocks, 3] (request, k0, k1) per score
                         // block, planned on the device when lengths are ragged (kv.seq_lens)
   PagedKV kv;           // decode only: paged pools (kv.block_table) or flat

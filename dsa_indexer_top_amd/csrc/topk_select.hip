@@ -515,8 +515,10 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
   // once every thread has it
   __shared__ int sh_cnt;
   if (threadIdx.x == 0) sh_cnt = p.cand_cnt[(size_t)r * p.cnt_stride];
-  uint32_t* gh = p.dec_hist + (size_t)r * kDecodeHistStride;
-  for (int i = threadIdx.x; i < kDecodeCntOffset; i += blockDim.x) gh[i] = 0u;
+  uint32_t* gh = p.dec_hist + (size_t)r * kDecodeHistRow;
+  static_assert(kDecodeCntOffset % 4 == 0 && kDecodeHistStride % 4 == 0, "16-byte clears");
+  for (int i = threadIdx.x; i < kDecodeHistRow / 4; i += blockDim.x)
+    if (i != kDecodeCntOffset / 4) ((uint4*)gh)[i] = make_uint4(0u, 0u, 0u, 0u);  // all but the counter's 16 bytes
   __syncthreads();
   const int cnt = sh_cnt;
   if (threadIdx.x == 0) gh[kDecodeCntOffset] = 0u;
@@ -900,7 +902,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     step(buf1, ksc1, base + kDecodeBlockKeys);
   }
   __syncthreads();
-  uint32_t* gh = p.dec_hist + (size_t)b * kDecodeHistStride;
+  uint32_t* gh = p.dec_hist + (size_t)b * kDecodeHistRow + (blockIdx.x % kDecodeHistCopies) * kDecodeHistStride;
   for (int i = threadIdx.x; i < kDecodeHistBins; i += 256) {
     const uint32_t c = hist[i];
     if (c) atomicAdd(&gh[i], c);
@@ -916,17 +918,27 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
   if ((threadIdx.x & 3) == 0 && cs) atomicAdd(&gh[kDecodeHistBins + (threadIdx.x >> 2)], cs);
 }
 
-// Threshold bin of a request's histogram gh (fine bins, then coarse bins) by
-// one wave: the largest T with count(bins >= T) >= k_eff, found in the
-// coarse bins first and then among the 64 fine bins of the coarse bin found.
+// Threshold bin of a request's histogram gh (its copies, each fine bins then
+// coarse bins) by one wave: the largest T with count(bins >= T) >= k_eff,
+// found in the coarse bins first and then among the 64 fine bins of the
+// coarse bin found.
+__device__ uint32_t sum_copies(const uint32_t* __restrict__ gh, int i) {
+  uint32_t v[kDecodeHistCopies];
+#pragma unroll
+  for (int c = 0; c < kDecodeHistCopies; ++c) v[c] = gh[c * kDecodeHistStride + i];
+  uint32_t s = 0u;
+#pragma unroll
+  for (int c = 0; c < kDecodeHistCopies; ++c) s += v[c];
+  return s;
+}
 __device__ int wave_threshold_bin(const uint32_t* __restrict__ gh, int k_eff) {
   const int lane = lane_id();
-  const uint32_t c = gh[kDecodeHistBins + kDecodeCoarseBins - 1 - lane];  // lane 0: top coarse bin
+  const uint32_t c = sum_copies(gh, kDecodeHistBins + kDecodeCoarseBins - 1 - lane);  // lane 0: top coarse bin
   const uint32_t ci = wave_incl_scan(c);
   const int L = uniform_i(__builtin_ctzll(ballot(ci >= (uint32_t)k_eff)));
   const uint32_t above = __shfl(ci - c, L, 64);  // keys in coarse bins above it
   const int cb = kDecodeCoarseBins - 1 - L;
-  const uint32_t f = gh[64 * cb + 63 - lane];
+  const uint32_t f = sum_copies(gh, 64 * cb + 63 - lane);
   const uint32_t fi = wave_incl_scan(f) + above;
   const int L2 = uniform_i(__builtin_ctzll(ballot(fi >= (uint32_t)k_eff)));
   return 64 * cb + 63 - L2;
@@ -947,7 +959,7 @@ __global__ __launch_bounds__(256) void decode_collect_kernel(IndexerParams p) {
   __shared__ int sh_tbin;
   if (threadIdx.x < kWave) {
     const int k_eff = min(p.topk, n_valid);
-    const int tb = wave_threshold_bin(p.dec_hist + (size_t)b * kDecodeHistStride, k_eff);
+    const int tb = wave_threshold_bin(p.dec_hist + (size_t)b * kDecodeHistRow, k_eff);
     if (threadIdx.x == 0) sh_tbin = tb;
   }
   __syncthreads();
@@ -1024,7 +1036,7 @@ hipError_t launch_indexer_decode(const IndexerParams& p, hipStream_t s) {
   // ragged score blocks; a later F layer of a stack finds them zero (the
   // finalize kernel clears its request's row) and the plan built
   if (!p.skip_prepare) {
-    const size_t nz = (size_t)p.B * kDecodeHistStride;
+    const size_t nz = (size_t)p.B * kDecodeHistRow;
     hipLaunchKernelGGL(decode_prepare_kernel, dim3((unsigned)std::min<size_t>((nz + 255) / 256, 1024)), dim3(256), 0,
                        s, p, nz, p.B + kDecodeTargetBlocks);
   }
