@@ -10,12 +10,17 @@ selection kernel) with inputs resident in HBM; value = L / step time.
 `roofline` is for the dominant kernel (the fused score + streaming-filter
 kernel): its algorithmic work is L(L+1)/2 * H_I * d_I * 2 flop per launch (the
 causal triangle only), timed live with HIP events recorded by the library on
-the stream it launches on. `cpu_baseline` times the fp64 CPU oracle on a
-bounded sample of the same layer's query rows and extrapolates by the number of
-causal keys. `extra` adds the bf16 200K layer, the 47-layer F/S prefill stack at
-L = 61440 (all-F, index_topk_freq 2 and 4), decode at 200K context and paged
-decode of 32 requests with ragged context lengths up to 200K, and the
-cross-layer top-k overlap of 47 layers.
+the stream it launches on; `peak` is the published one and `peak_measured` the
+rate of a dense MFMA loop of the same dtype on this GPU. `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same layer's query rows and
+extrapolates by the number of causal keys. `extra` adds the measured peaks
+(MFMA loops, HBM copy and read), the single-layer L = 10240 bf16 layer with
+the CPU oracle timed over all of it, the bf16 200K layer, the 47-layer F/S
+prefill stack at L = 61440 (all-F, index_topk_freq 2 and 4) and at 200K (all-F,
+the seeded 12-F pattern, and that pattern prefilled in chunks of 25000 rows),
+decode at 200K context (per-kernel times warm and over rotating layer sets)
+and paged decode of 32 requests with ragged context lengths up to 200K, and
+the cross-layer top-k overlap of 47 layers.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -33,6 +38,7 @@ METRIC = "indexer+top-k queries/sec & fraction of MFMA peak at 200K; stack prefi
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_prefill_fp8_L200000_traffic.json")
+PEAK_LIB = os.path.join(ROOT, "dsa_indexer_top_amd", "libdsa_peak.so")
 KERNEL_SOURCES = ["dsa_indexer_top_amd/csrc/indexer_prefill.hip", "dsa_indexer_top_amd/csrc/dsa_device.h"]
 
 
@@ -92,17 +98,120 @@ def traffic_for_current_kernel():
     return t.get("traffic_bytes_per_launch")
 
 
+def cpu_info():
+    """CPU model, the threads this process may use and the BLAS numpy calls."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{k: p.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer", "architecture")}
+                for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(),
+            "cpus_available": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "blas": blas}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        return 1
+
+
+def measured_peaks(torch):
+    """Rates of the probes in libdsa_peak.so on this GPU (best of 3 timed
+    launches after one untimed): dense MFMA loops in bf16 and fp8 (two
+    workgroups of four waves per CU, four independent accumulators per wave),
+    and an HBM copy and read of 2 GiB with 16-byte accesses."""
+    import ctypes
+    lib = ctypes.CDLL(PEAK_LIB)
+    lib.dsa_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.dsa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    lib.dsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_ms(launch, reps=3):
+        launch()
+        ms = []
+        for _ in range(reps):
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return min(ms)
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"cus": cus}
+    out = torch.empty(2 * cus * 256, dtype=torch.float32, device="cuda")
+    for code, name, iters in ((0, "bf16", 40000), (1, "fp8", 20000)):
+        flop = ctypes.c_double()
+
+        def run():
+            if lib.dsa_peak_mfma(code, 2 * cus, iters, out.data_ptr(), ctypes.byref(flop), stream) != 0:
+                raise RuntimeError("dsa_peak_mfma failed")
+        ms = best_ms(run)
+        res[f"mfma_{name}_TFLOPs"] = flop.value / (ms * 1e-3) / 1e12
+    n = 2 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    red = torch.empty(16384, dtype=torch.int32, device="cuda")
+    copy_best = read_best = 0.0
+    for blocks in (2048, 4096, 8192):
+        def cp():
+            if lib.dsa_peak_copy(src.data_ptr(), dst.data_ptr(), n, blocks, stream) != 0:
+                raise RuntimeError("dsa_peak_copy failed")
+
+        def rd():
+            if lib.dsa_peak_read(src.data_ptr(), n, blocks, red.data_ptr(), stream) != 0:
+                raise RuntimeError("dsa_peak_read failed")
+        copy_best = max(copy_best, 2 * n / best_ms(cp) / 1e6)
+        read_best = max(read_best, n / best_ms(rd) / 1e6)
+    res["hbm_copy_GBps"] = copy_best
+    res["hbm_read_GBps"] = read_best
+    res["published"] = {"mfma_bf16_TFLOPs": PEAK_TFLOPS["bf16"], "mfma_fp8_TFLOPs": PEAK_TFLOPS["fp8"],
+                        "hbm_GBps": PEAK_HBM_GBS}
+    log(f"measured peaks: MFMA bf16 {res['mfma_bf16_TFLOPs']:.0f} TFLOP/s, fp8 {res['mfma_fp8_TFLOPs']:.0f} "
+        f"TFLOP/s; HBM copy {copy_best:.0f} GB/s, read {read_best:.0f} GB/s")
+    del src, dst, red, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_c2_full(L=10240, topk=2048):
+    """The fp64 oracle over every query row of the L = 10240 bf16 layer
+    (scores and top-k), timed in full on this host."""
+    import oracle
+    from dsa_inputs import host_bits, make_indexer_inputs
+    inp = make_indexer_inputs(1, L, L, 64, 128, config=2, dtype="bf16", w_std=0.125)
+    q, k, w = host_bits(inp.q), host_bits(inp.k), host_bits(inp.w)
+    t0 = time.perf_counter()
+    oracle.indexer_topk(q, k, w, topk)
+    t = time.perf_counter() - t0
+    log(f"CPU oracle, L={L} bf16 layer in full: {t:.1f} s")
+    return {"value": L / t, "unit": "queries/s", "seconds": t, "cores": blas_threads(), "kind": "oracle",
+            "sample": f"all {L} query rows of the layer (scores and top-k), not extrapolated", **cpu_info()}
+
+
 def cpu_baseline(inp_host, L, topk, budget_s):
     """Times the fp64 oracle on seeded random query rows of the layer until the
     time budget is spent, and extrapolates to the whole layer by causal keys."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
+    threads = blas_threads()
     rng = np.random.default_rng(2024)
     order = rng.permutation(L)
     done_rows, done_keys, spent = 0, 0, 0.0
@@ -122,14 +231,17 @@ def cpu_baseline(inp_host, L, topk, budget_s):
     return {"value": L / est_s, "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": (f"{done_rows} seeded-random query rows of the same layer ({done_keys} causal "
                        f"keys, {spent:.1f} s of fp64 oracle: scores + top-k), extrapolated to all "
-                       f"{L} rows by causal-key count (layer estimate {est_s:.0f} s)")}
+                       f"{L} rows by causal-key count (layer estimate {est_s:.0f} s)"), **cpu_info()}
 
 
-def stack_bench(dsa, torch, L, n_layers, topk, steps, warmup, config=3, dtype="bf16", patterns=None):
+def stack_bench(dsa, torch, L, n_layers, topk, steps, warmup, config=3, dtype="bf16", patterns=None,
+                chunked=None):
     """47-layer prefill stack, per-layer tensors seeded independently, one shared
     index buffer. patterns: list of (name, run kwargs); default all-F vs
     index_topk_freq 2 and 4. Reports each pattern's best wall time and mean
-    per-layer event times of its F and S layers."""
+    per-layer event times of its F and S layers. chunked: list of (name, run
+    kwargs, chunk_rows): the same layers prefilled chunk by chunk (each chunk's
+    rows over the keys up to its last row, a per-chunk index buffer)."""
     from dsa_inputs import make_attn_inputs, make_indexer_inputs
     if patterns is None:
         patterns = [("all_F", {}), ("freq2", {"freq": 2}), ("freq4", {"freq": 4})]
@@ -162,7 +274,26 @@ def stack_bench(dsa, torch, L, n_layers, topk, steps, warmup, config=3, dtype="b
         log(f"stack L={L} {name}: {min(times):.3f} s")
     for name, _ in patterns[1:]:
         res[name]["speedup_vs_all_F"] = res["all_F"]["time_s"] / res[name]["time_s"]
-    del st, layers
+    del st
+    torch.cuda.empty_cache()
+    for name, kw, rows in chunked or []:
+        stc = dsa.LayerStack(layers, topk, shared_out=True, chunk_rows=rows)
+        for _ in range(warmup):
+            stc.run(**kw)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(steps):
+            t0 = time.perf_counter()
+            stc.run(**kw)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        pat = dsa.resolve_pattern(n_layers, kw.get("pattern"), kw.get("freq", 0))
+        res[name] = {"pattern": pat, "pattern_F": pat.count("F"), "chunk_rows": rows,
+                     "chunks": (L + rows - 1) // rows, "time_s": min(times)}
+        log(f"stack L={L} {name} (chunks of {rows}): {min(times):.3f} s")
+        del stc
+        torch.cuda.empty_cache()
+    del layers
     torch.cuda.empty_cache()
     return res
 
@@ -197,6 +328,19 @@ def decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, config=4):
             a_ms += eva[0].elapsed_time(eva[1]) / steps
     idx_bytes = B * T * 128 * 2 + B * T * 4                 # k_idx read + score keys written
     att_bytes = B * topk * 2 * 128 * 2                      # gathered K and V rows
+    # cold: each call on the next distinct layer set (B = 1: 47 sets of 154 MB;
+    # B = 32: two sets of 4.9 GB), so no call finds its inputs in the 256 MB
+    # memory-side cache
+    kc_ms = ac_ms = 0.0
+    n_cold = max(2 * n_sets, 8) if B > 1 else n_sets
+    for i in range(n_cold + 1):
+        s_ = sets[i % n_sets]
+        r = dsa.indexer_scores_topk(s_["q_idx"], s_["k_idx"], s_["w"], topk, phase_events=evi)
+        dsa.sparse_attn(s_["q"], s_["k"], s_["v"], r.idx, phase_events=eva)
+        torch.cuda.synchronize()
+        if i >= 1:
+            kc_ms += evi[0].elapsed_time(evi[1]) / n_cold
+            ac_ms += eva[0].elapsed_time(eva[1]) / n_cold
     st = dsa.LayerStack(layers, topk, shared_out=True)
     for _ in range(warmup):
         st.run(pat)
@@ -212,10 +356,16 @@ def decode_bench(dsa, torch, B, T, n_layers, topk, steps, warmup, config=4):
            "indexer_kernel_ms": k_ms, "indexer_hbm_GBps": idx_bytes / k_ms / 1e6,
            "indexer_hbm_frac": idx_bytes / k_ms / 1e6 / PEAK_HBM_GBS,
            "attn_ms": a_ms, "attn_gather_GBps": att_bytes / a_ms / 1e6,
+           "attn_gather_hbm_frac": att_bytes / a_ms / 1e6 / PEAK_HBM_GBS,
+           "cold": {"sets": n_sets, "calls": n_cold,
+                    "indexer_kernel_ms": kc_ms, "indexer_hbm_GBps": idx_bytes / kc_ms / 1e6,
+                    "indexer_hbm_frac": idx_bytes / kc_ms / 1e6 / PEAK_HBM_GBS,
+                    "attn_ms": ac_ms, "attn_gather_GBps": att_bytes / ac_ms / 1e6,
+                    "attn_gather_hbm_frac": att_bytes / ac_ms / 1e6 / PEAK_HBM_GBS},
            "step_ms_47_layers": step * 1e3, "tok_per_s_per_request": 1.0 / step,
            "tok_per_s_total": B / step}
-    log(f"decode B={B}: indexer {k_ms:.3f} ms ({res['indexer_hbm_GBps']:.0f} GB/s), "
-        f"attn {a_ms:.3f} ms, 47-layer step {step*1e3:.2f} ms")
+    log(f"decode B={B}: indexer {k_ms:.3f} ms warm / {kc_ms:.3f} ms cold ({idx_bytes / kc_ms / 1e6:.0f} GB/s), "
+        f"attn {a_ms:.3f} ms warm / {ac_ms:.3f} ms cold, 47-layer step {step*1e3:.2f} ms")
     del st, layers, sets
     torch.cuda.empty_cache()
     return res
@@ -229,20 +379,30 @@ def decode_gather_bench(dsa, torch, B, T, topk, steps, warmup, config=4):
     from dsa_inputs import make_attn_inputs
     a = make_attn_inputs(B, 1, T, 16, 128, config=config, device="cuda")
     g = torch.Generator(device="cuda").manual_seed(1_000_000 * config + 13)
-    idx = torch.randint(0, T, (B, 1, topk), generator=g, device="cuda", dtype=torch.int32)
+    # four index sets: the warm figure repeats the first, the cold one rotates
+    # them (each call gathers rows the previous three calls did not touch)
+    idxs = [torch.randint(0, T, (B, 1, topk), generator=g, device="cuda", dtype=torch.int32) for _ in range(4)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ms = []
+    ms, cold = [], []
     for i in range(warmup + steps):
-        dsa.sparse_attn(a.q, a.k, a.v, idx, phase_events=ev)
+        dsa.sparse_attn(a.q, a.k, a.v, idxs[0], phase_events=ev)
         torch.cuda.synchronize()
         if i >= warmup:
             ms.append(ev[0].elapsed_time(ev[1]))
+    for i in range(1, 1 + 2 * len(idxs)):
+        dsa.sparse_attn(a.q, a.k, a.v, idxs[i % len(idxs)], phase_events=ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[1]))
     a_ms = sum(ms) / len(ms)
+    c_ms = sum(cold) / len(cold)
     att_bytes = B * topk * 2 * 128 * 2  # gathered K and V rows
     res = {"B": B, "context": T, "topk": topk, "attn_ms": a_ms, "attn_gather_GBps": att_bytes / a_ms / 1e6,
-           "attn_gather_hbm_frac": att_bytes / a_ms / 1e6 / PEAK_HBM_GBS}
-    log(f"decode attention B={B}: {a_ms * 1e3:.1f} us ({res['attn_gather_GBps']:.0f} GB/s of gathered rows)")
-    del a, idx
+           "attn_gather_hbm_frac": att_bytes / a_ms / 1e6 / PEAK_HBM_GBS,
+           "cold": {"index_sets": len(idxs), "attn_ms": c_ms, "attn_gather_GBps": att_bytes / c_ms / 1e6,
+                    "attn_gather_hbm_frac": att_bytes / c_ms / 1e6 / PEAK_HBM_GBS}}
+    log(f"decode attention B={B}: {a_ms * 1e3:.1f} us warm, {c_ms * 1e3:.1f} us cold "
+        f"({att_bytes / c_ms / 1e6:.0f} GB/s of gathered rows)")
+    del a, idxs
     torch.cuda.empty_cache()
     return res
 
@@ -362,14 +522,42 @@ def quant_bench(dsa, torch, L, steps):
             "hbm_frac": nbytes / ms / 1e6 / PEAK_HBM_GBS}
 
 
+def c2_bench(dsa, torch, steps, warmup, peaks=None, L=10240, topk=2048):
+    """The single-layer L = 10240 bf16 layer (H_I = 64, d_I = 128, k = 2048):
+    queries/s of the fused indexer + top-k step and the score kernel's MFMA
+    fraction (causal flop / kernel time) against the published and the
+    measured bf16 peak."""
+    from dsa_inputs import make_indexer_inputs
+    inp = make_indexer_inputs(1, L, L, 64, 128, config=2, dtype="bf16", w_std=0.125, device="cuda")
+    wall, k_ms, s_ms, _ = time_indexer(dsa, torch, inp, topk, steps, warmup)
+    flops = causal_flops(L, 64, 128)
+    a = flops / (k_ms * 1e-3) / 1e12
+    step_tf = flops / (wall * 1e-3) / 1e12
+    res = {"L": L, "dtype": "bf16", "topk": topk, "ms_per_step": wall, "queries_per_s": L / (wall * 1e-3),
+           "score_kernel_ms": k_ms, "select_kernel_ms": s_ms, "score_kernel_TFLOPs": a,
+           "mfma_frac": a / PEAK_TFLOPS["bf16"], "step_mfma_frac": step_tf / PEAK_TFLOPS["bf16"]}
+    if peaks:
+        res["mfma_frac_of_measured"] = a / peaks["mfma_bf16_TFLOPs"]
+        res["step_mfma_frac_of_measured"] = step_tf / peaks["mfma_bf16_TFLOPs"]
+    log(f"L={L} bf16: {wall:.3f} ms/step ({L / (wall * 1e-3):.0f} queries/s), score kernel {k_ms:.3f} ms "
+        f"({a:.0f} TFLOP/s, {a / PEAK_TFLOPS['bf16']:.3f} of peak)")
+    del inp
+    torch.cuda.empty_cache()
+    return res
+
+
 def stack200k(dsa, torch, L, topk, args):
     """The 47-layer stack at L = 200000 with the fp8 indexer: all-F vs a seeded
     pattern with 12 F layers (layer 0 and 11 of layers 1..46)."""
     from dsa_inputs import seeded_pattern
     pat = seeded_pattern(47, 12, seed=1_000_000 * 5 + 9)
-    return {"L": L, "layers": 47, "dtype": "fp8 indexer, bf16 attention", "attn": "16 heads, d=128, 1 KV head",
-            **stack_bench(dsa, torch, L, 47, topk, 1, 1, config=5, dtype="fp8",
-                          patterns=[("all_F", {}), ("seeded_quarter_F", {"pattern": pat})])}
+    res = {"L": L, "layers": 47, "dtype": "fp8 indexer, bf16 attention", "attn": "16 heads, d=128, 1 KV head",
+           **stack_bench(dsa, torch, L, 47, topk, 1, 1, config=5, dtype="fp8",
+                         patterns=[("all_F", {}), ("seeded_quarter_F", {"pattern": pat})],
+                         chunked=[("seeded_quarter_F_chunked", {"pattern": pat}, 25000)])}
+    res["seeded_quarter_F_chunked"]["time_vs_one_shot"] = (res["seeded_quarter_F_chunked"]["time_s"]
+                                                           / res["seeded_quarter_F"]["time_s"])
+    return res
 
 
 def main():
@@ -385,7 +573,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline + CPU baseline only")
     ap.add_argument("--stack-L", type=int, default=61440)
     ap.add_argument("--stack-layers", type=int, default=47)
-    ap.add_argument("--only", choices=["stack", "stack200k", "decode", "paged", "quant", "overlap"], default=None,
+    ap.add_argument("--only", choices=["stack", "stack200k", "decode", "paged", "quant", "overlap", "peaks", "c2"],
+                    default=None,
                     help="run only the stack or only the decode measurement and print its JSON "
                          "(for profiling one part; not the benchmark line)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -431,6 +620,12 @@ def main():
         res["decode_attn_B256"] = decode_gather_bench(dsa, torch, 256, 200000, topk, max(3, args.steps), 2)
         print(json.dumps(res), flush=True)
         return
+    if args.only == "peaks":
+        print(json.dumps(measured_peaks(torch)), flush=True)
+        return
+    if args.only == "c2":
+        print(json.dumps(c2_bench(dsa, torch, max(5, args.steps), args.warmup)), flush=True)
+        return
     if args.only == "overlap":
         print(json.dumps(overlap_bench(dsa, torch, max(2, args.steps))), flush=True)
         return
@@ -438,6 +633,9 @@ def main():
         print(json.dumps(paged_decode_bench(dsa, torch, 32, 200000, 47, topk, args.steps, 2)), flush=True)
         return
 
+    peaks = None
+    if not (args.no_extra or args.quick):
+        peaks = measured_peaks(torch)
     log(f"generating the L={L} {args.dtype} layer")
     inp = make_indexer_inputs(1, L, L, H, D, config=5, dtype=args.dtype, w_std=0.125, device="cuda")
     torch.cuda.synchronize()
@@ -470,7 +668,9 @@ def main():
                      "traffic": traffic_for_current_kernel() if (args.dtype == "fp8" and L == 200000)
                      else None,
                      "kernel": "indexer_prefill_kernel", "kernel_ms": k_ms,
-                     "flop_per_launch": flops},
+                     "flop_per_launch": flops,
+                     "peak_measured": peaks[f"mfma_{args.dtype}_TFLOPs"] if peaks else None,
+                     "frac_of_measured": achieved / peaks[f"mfma_{args.dtype}_TFLOPs"] if peaks else None},
         "select_kernel_ms": s_ms,
     }
     if not args.no_cpu:
@@ -482,15 +682,23 @@ def main():
     torch.cuda.empty_cache()
 
     if not (args.no_extra or args.quick):
-        extra = {}
+        extra = {"measured_peaks": peaks}
+        log("L=10240 bf16 layer")
+        extra["C2_L10240_bf16"] = c2_bench(dsa, torch, max(10, 2 * args.steps), args.warmup, peaks)
+        if not args.no_cpu:
+            extra["cpu_oracle_L10240_bf16_full"] = cpu_c2_full()
         other = "bf16" if args.dtype == "fp8" else "fp8"
         log(f"generating the L={L} {other} layer")
         inp2 = make_indexer_inputs(1, L, L, H, D, config=5, dtype=other, w_std=0.125, device="cuda")
         w2, k2, s2, _ = time_indexer(dsa, torch, inp2, topk, max(2, args.steps // 2), 1)
         a2 = flops / (k2 * 1e-3) / 1e12
+        st2 = flops / (w2 * 1e-3) / 1e12
         extra[f"{other}_L{L}"] = {"ms_per_step": w2, "queries_per_s": L / (w2 * 1e-3),
                                   "score_kernel_ms": k2, "select_kernel_ms": s2,
                                   "TFLOPs": a2, "mfma_frac": a2 / PEAK_TFLOPS[other],
+                                  "step_mfma_frac": st2 / PEAK_TFLOPS[other],
+                                  "mfma_frac_of_measured": a2 / peaks[f"mfma_{other}_TFLOPs"],
+                                  "step_mfma_frac_of_measured": st2 / peaks[f"mfma_{other}_TFLOPs"],
                                   "frac_of_bf16_peak": a2 / PEAK_TFLOPS["bf16"]}
         log(f"{other}: {w2:.2f} ms/step, kernel {k2:.2f} ms ({a2:.1f} TFLOP/s)")
         del inp2
@@ -512,6 +720,15 @@ def main():
         log("paged ragged decode B=32")
         extra["decode_paged_ragged_B32"] = paged_decode_bench(dsa, torch, 32, 200000, 47, topk, args.steps, 2)
         extra["topk_overlap_47_layers"] = overlap_bench(dsa, torch, max(2, args.steps))
+        # HBM-bound figures against the rates measured on this GPU as well
+        rd, cp = peaks["hbm_read_GBps"], peaks["hbm_copy_GBps"]
+        for key in ("decode_B1", "decode_B32"):
+            for part in (extra[key], extra[key]["cold"]):
+                part["indexer_frac_of_measured_read"] = part["indexer_hbm_GBps"] / rd
+                part["attn_gather_frac_of_measured_read"] = part["attn_gather_GBps"] / rd
+        for part in (extra["decode_attn_B256"], extra["decode_attn_B256"]["cold"]):
+            part["attn_gather_frac_of_measured_read"] = part["attn_gather_GBps"] / rd
+        extra["quantize_fp8_q_idx"]["frac_of_measured_copy"] = extra["quantize_fp8_q_idx"]["hbm_GBps"] / cp
         result["extra"] = extra
     print(json.dumps(result), flush=True)
 

@@ -1,4 +1,5 @@
-"""Builds libdsa.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc."""
+"""Builds libdsa.so (HIP kernels for gfx950 + the C ABI) and libdsa_peak.so (the
+rate probes the benchmark measures peaks with) in-tree with hipcc."""
 from __future__ import annotations
 
 import os
@@ -13,6 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
+PEAK_LIB = os.path.join(PKG, "libdsa_peak.so")
 
 SOURCES = ["dsa_api.cpp", "indexer_prefill.hip", "topk_select.hip", "sparse_attn.hip", "quant.hip", "paged.hip", "overlap.hip"]
 
@@ -44,18 +46,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source and links libdsa.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     # --no-undefined: a kernel whose host stub was not emitted fails here, not at load
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source, links libdsa.so and libdsa_peak.so; returns the
+    path of libdsa.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + ["peak.hip"]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PEAK_LIB)
     return LIB
 
 

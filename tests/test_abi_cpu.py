@@ -23,8 +23,8 @@ def lib():
     return dsa.load()
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "dsa.h")).read()
+def _declared_functions(header="dsa.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", src)))
 
@@ -35,6 +35,27 @@ def test_exports_every_declared_symbol(lib):
     for name in declared:
         assert hasattr(lib, name), name
     assert lib.dsa_abi_version() == 1
+
+
+def test_peak_probe_library_exports():
+    """The rate-probe library the benchmark measures peaks with loads and
+    exports what include/dsa_peak.h declares; invalid arguments are refused
+    before any launch."""
+    path = os.path.join(ROOT, "dsa_indexer_top_amd", "libdsa_peak.so")
+    plib = ctypes.CDLL(path)
+    declared = _declared_functions("dsa_peak.h")
+    assert declared == ["dsa_peak_copy", "dsa_peak_mfma", "dsa_peak_read"]
+    for name in declared:
+        assert hasattr(plib, name), name
+    plib.dsa_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    plib.dsa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    plib.dsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert plib.dsa_peak_mfma(2, 1, 1, 16, None, None) == 1          # unknown dtype
+    assert plib.dsa_peak_mfma(0, 0, 1, 16, None, None) == 1          # no blocks
+    assert plib.dsa_peak_copy(16, 32, 17, 1, None) == 1              # not a multiple of 16
+    assert plib.dsa_peak_copy(None, 32, 16, 1, None) == 1
+    assert plib.dsa_peak_read(16, 16, 1, None, None) == 1            # no output
 
 
 def _c_layout(tmp_path, struct, fields):
