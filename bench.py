@@ -133,7 +133,8 @@ def measured_peaks(torch):
     """Rates of the probes in libdsa_peak.so on this GPU (best of 3 timed
     launches after one untimed): dense MFMA loops in bf16 and fp8 (two
     workgroups of four waves per CU, four independent accumulators per wave),
-    and an HBM copy and read of 2 GiB with 16-byte accesses."""
+    and an HBM copy and read of 2 GiB with 16-byte nontemporal accesses (the
+    best of four grid sizes)."""
     import ctypes
     lib = ctypes.CDLL(PEAK_LIB)
     lib.dsa_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -170,7 +171,7 @@ def measured_peaks(torch):
     dst = torch.empty_like(src)
     red = torch.empty(16384, dtype=torch.int32, device="cuda")
     copy_best = read_best = 0.0
-    for blocks in (2048, 4096, 8192):
+    for blocks in (1024, 2048, 4096, 8192):
         def cp():
             if lib.dsa_peak_copy(src.data_ptr(), dst.data_ptr(), n, blocks, stream) != 0:
                 raise RuntimeError("dsa_peak_copy failed")

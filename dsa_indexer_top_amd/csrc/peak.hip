@@ -9,6 +9,7 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Four independent accumulator chains per wave keep the matrix pipe fed
 // across each MFMA's latency; two workgroups of four waves per CU put two
@@ -53,32 +54,38 @@ __global__ __launch_bounds__(256) void mfma_loop(int iters, float* out) {
   out[(size_t)blockIdx.x * 256 + t] = s;
 }
 
-// Four 16-byte words per thread per round, so every wave has four loads in
-// flight before its stores.
-__global__ __launch_bounds__(256) void copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
+// U 16-byte words per thread per round, loaded (nontemporal: read once)
+// before any is used, so every wave keeps U loads in flight.
+constexpr int kCopyU = 8;
+constexpr int kReadU = 16;
+
+__global__ __launch_bounds__(256) void copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
   const size_t stride = (size_t)gridDim.x * 256;
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+  for (; i + (kCopyU - 1) * stride < n; i += kCopyU * stride) {
+    u32x4 v[kCopyU];
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kCopyU; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
   }
   for (; i < n; i += stride) dst[i] = src[i];
 }
 
-__global__ __launch_bounds__(256) void read16(const uint4* __restrict__ src, size_t n, uint32_t* out) {
+__global__ __launch_bounds__(256) void read16(const u32x4* __restrict__ src, size_t n, uint32_t* out) {
   const size_t stride = (size_t)gridDim.x * 256;
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   uint32_t x = 0u;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  for (; i + (kReadU - 1) * stride < n; i += kReadU * stride) {
+    u32x4 v[kReadU];
+#pragma unroll
+    for (int u = 0; u < kReadU; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kReadU; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (; i < n; i += stride) {
-    const uint4 a = src[i];
-    x ^= a.x ^ a.y ^ a.z ^ a.w;
+    const u32x4 a = src[i];
+    x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
   }
   __shared__ uint32_t red[256];
   red[threadIdx.x] = x;
@@ -108,13 +115,13 @@ extern "C" int dsa_peak_mfma(int dtype, int blocks, int iters, float* out, doubl
 
 extern "C" int dsa_peak_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
   if (!src || !dst || bytes % 16 || blocks < 1 || ((uintptr_t)src | (uintptr_t)dst) % 16) return 1;
-  hipLaunchKernelGGL(copy16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (uint4*)dst,
+  hipLaunchKernelGGL(copy16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, (u32x4*)dst,
                      bytes / 16);
   return launched();
 }
 
 extern "C" int dsa_peak_read(const void* src, size_t bytes, int blocks, uint32_t* out, void* stream) {
   if (!src || !out || bytes % 16 || blocks < 1 || (uintptr_t)src % 16) return 1;
-  hipLaunchKernelGGL(read16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, bytes / 16, out);
+  hipLaunchKernelGGL(read16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, bytes / 16, out);
   return launched();
 }

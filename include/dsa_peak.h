@@ -27,12 +27,14 @@ extern "C" {
 int dsa_peak_mfma(int dtype, int blocks, int iters, float* out, double* flop, void* stream);
 
 /* HBM copy: dst[i] = src[i] for `bytes` bytes (a multiple of 16, both
- * 16-byte aligned) with 16-byte loads and stores, grid-stride over
- * `blocks` workgroups of 256 threads. Moves 2 * bytes. */
+ * 16-byte aligned) with 16-byte nontemporal loads and stores, eight in
+ * flight per thread, grid-stride over `blocks` workgroups of 256 threads.
+ * Moves 2 * bytes. */
 int dsa_peak_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream);
 
-/* HBM read: every 16-byte word of src (bytes a multiple of 16) is read and
- * folded (xor) into out[block] (blocks words), so the loads are kept. */
+/* HBM read: every 16-byte word of src (bytes a multiple of 16) is read
+ * (nontemporal, sixteen in flight per thread) and folded (xor) into
+ * out[block] (blocks words), so the loads are kept. */
 int dsa_peak_read(const void* src, size_t bytes, int blocks, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
