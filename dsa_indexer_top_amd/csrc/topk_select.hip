@@ -253,6 +253,15 @@ constexpr int kMaxTopk = 2048;
 // entries ranked below `take` are written straight to their output slots. If
 // a bucket holds more than kBucketMaxRun entries (heavy ties), it returns
 // false before writing any output.
+// NARROW: a list longer than 1.5 * take (a prefill row that never filled its
+// list and holds every causal key, or one refilled far past take since its
+// last shrink) first gets a counting-only pass over the same buckets; the end
+// of the bucket holding rank take - 1 bounds the keys that can reach the
+// top-k from below, and the ranking pass then buckets only the entries at or
+// above that bound, over their own key range. Every other entry ranks below them, so their ranks among themselves
+// are the list's ranks. Without it, such a list's 2^kBucketBits buckets span
+// its whole key range and crowd the entries around rank take - 1 into a few
+// buckets, whose members each compare with the whole bucket.
 static_assert(kFinNTPrefill == kFinNTDecode, "one bucket layout for both finalize kernels");
 constexpr int kBucketPer = kMaxC / kFinNTDecode;  // entries per thread
 constexpr int kBucketEarly = kBucketPer / 2;      // of them loaded before the count is known
@@ -278,7 +287,7 @@ __device__ void bucket_load(BucketEntries& v, const uint32_t* __restrict__ ck, c
   }
 }
 
-template <int kBucketBits, int H>
+template <int kBucketBits, int H, bool NARROW>
 __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEntries& v, int cnt, int take,
                                  uint64_t* word, uint32_t* base, int* scratch) {
   constexpr int kBuckets = 1 << kBucketBits;
@@ -312,12 +321,41 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
     umin = min(umin, sh_min[q]);
     umax = max(umax, sh_max[q]);
   }
-  const uint32_t range = umax - umin;
-  const int shift = (range >> kBucketBits) ? 32 - __builtin_clz(range) - kBucketBits : 0;  // range >> shift < kBuckets
+  uint32_t lo = umin;  // entries with a key >= lo take part
+  int shift = (umax - lo) >> kBucketBits ? 32 - __builtin_clz(umax - lo) - kBucketBits : 0;  // range >> shift < kBuckets
+  if (NARROW && 2 * cnt > 3 * take && shift > 0) {  // uniform
+    __shared__ uint32_t sh_lo;
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (threadIdx.x + e * kFinNTDecode < cnt) atomicAdd(&base[(umax - v.u[e]) >> shift], 1u);
+    __syncthreads();
+    uint32_t c[BPT], local = 0u;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      c[q] = base[BPT * threadIdx.x + q];
+      local += c[q];
+    }
+    int all;
+    uint32_t pre = (uint32_t)block_excl_scan((int)local, scratch, &all);  // its barriers order the reads above
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      if (c[q] && pre <= (uint32_t)(take - 1) && (uint32_t)(take - 1) < pre + c[q]) {
+        // the lowest key bucket BPT*t + q spans (umin if that is below it)
+        const uint64_t span = (uint64_t)(BPT * threadIdx.x + q + 1) << shift;
+        sh_lo = span > (uint64_t)(umax - umin) ? umin : (uint32_t)(umax - span + 1u);
+      }
+      pre += c[q];
+      base[BPT * threadIdx.x + q] = 0u;
+    }
+    __syncthreads();
+    lo = sh_lo;
+    shift = (umax - lo) >> kBucketBits ? 32 - __builtin_clz(umax - lo) - kBucketBits : 0;
+  }
   uint32_t slot[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e)
-    slot[e] = threadIdx.x + e * kFinNTDecode < cnt ? atomicAdd(&base[(umax - v.u[e]) >> shift], 1u) : 0u;
+    slot[e] = threadIdx.x + e * kFinNTDecode < cnt && v.u[e] >= lo ? atomicAdd(&base[(umax - v.u[e]) >> shift], 1u)
+                                                                   : 0u;
   __syncthreads();
   uint32_t c[BPT], local = 0u, run = 0u;
 #pragma unroll
@@ -329,8 +367,8 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) run = max(run, (uint32_t)__shfl_xor((int)run, d, 64));
   if (lane == 0) sh_run[w] = run;
-  int total;
-  uint32_t pre = (uint32_t)block_excl_scan((int)local, scratch, &total);  // its barriers order the reads above
+  int n_in;  // entries taking part
+  uint32_t pre = (uint32_t)block_excl_scan((int)local, scratch, &n_in);  // its barriers order the reads above
   // buckets are laid out in rank order, so the entries that can rank below
   // `take` are the prefix up to the end of the bucket holding rank take - 1
   __shared__ int sh_prefix;
@@ -345,10 +383,10 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
   for (int q = 1; q < kSortWaves; ++q) max_run = max(max_run, (int)sh_run[q]);  // uniform
   __syncthreads();
   if (max_run > kBucketMaxRun) return false;
-  const int prefix = sh_prefix;  // take <= cnt, so one bucket holds rank take - 1
+  const int prefix = sh_prefix;  // take <= the entries taking part, so one bucket holds rank take - 1
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    if (threadIdx.x + e * kFinNTDecode < cnt) {
+    if (threadIdx.x + e * kFinNTDecode < cnt && v.u[e] >= lo) {
       const int s0 = (int)base[(umax - v.u[e]) >> shift];
       if (s0 < prefix) word[s0 + slot[e]] = ((uint64_t)v.u[e] << 32) | (uint32_t)~(uint32_t)v.x[e];
     }
@@ -394,10 +432,10 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
     int s0[H], len[H];
 #pragma unroll
     for (int q = 0; q < H; ++q) {
-      const bool in = threadIdx.x + q * kFinNTDecode < cnt;
+      const bool in = threadIdx.x + q * kFinNTDecode < cnt && v.u[q] >= lo;
       const uint32_t bk = in ? (umax - v.u[q]) >> shift : 0u;
       s0[q] = (int)base[bk];
-      len[q] = in && s0[q] < prefix ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : cnt) - s0[q] : 0;
+      len[q] = in && s0[q] < prefix ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : n_in) - s0[q] : 0;
       mine[q] = ((uint64_t)v.u[q] << 32) | (uint32_t)~(uint32_t)v.x[q];
     }
     rank_group(mine, s0, len);
@@ -412,7 +450,7 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
         mine[q] = word[in ? j : 0];
         const uint32_t bk = (umax - (uint32_t)(mine[q] >> 32)) >> shift;
         s0[q] = (int)base[in ? bk : 0u];
-        len[q] = in ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : cnt) - s0[q] : 0;
+        len[q] = in ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : n_in) - s0[q] : 0;
       }
       rank_group(mine, s0, len);
     }
@@ -454,7 +492,7 @@ __global__ __launch_bounds__(kFinNTPrefill) __attribute__((amdgpu_waves_per_eu(4
   const int take = min(k_eff, cnt);
   if (cnt >= 1) {
     bucket_load(ent, ck, ci, kBucketEarly, kBucketPer, cnt);
-    if (bucket_rank_topk<kBits, 4>(p, r, ent, cnt, take, (uint64_t*)lds, (uint32_t*)(lds + kMaxC * 8), scratch))
+    if (bucket_rank_topk<kBits, 4, true>(p, r, ent, cnt, take, (uint64_t*)lds, (uint32_t*)(lds + kMaxC * 8), scratch))
       return;
   }
   for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
@@ -528,7 +566,7 @@ __global__ __launch_bounds__(kFinNTDecode) void decode_finalize_kernel(FinalizeP
     take = min(k_eff, cnt);  // cnt >= k_eff by construction
     if (cnt >= 1) {
       bucket_load(ent, ck, ci, kBucketEarly, kBucketPer, cnt);  // the rest (zeros past the end)
-      if (bucket_rank_topk<kBits, 8>(p, r, ent, cnt, take, (uint64_t*)lds, (uint32_t*)(lds + kMaxC * 8), scratch))
+      if (bucket_rank_topk<kBits, 8, false>(p, r, ent, cnt, take, (uint64_t*)lds, (uint32_t*)(lds + kMaxC * 8), scratch))
         return;
     }
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) skey[i] = ck[i];
