@@ -236,7 +236,7 @@ dsa_status dsa_indexer_scores_topk(const dsa_indexer_args *args, void *stream);
  * that each GPU holds from the first call on it until the process ends; a
  * shape whose dsa_indexer_workspace_size exceeds it returns DSA_ERR_WORKSPACE
  * before anything is enqueued (e.g. decode of B = 32 requests over 200K-token
- * contexts at topk = 2048 needs about 28 MB; prefill needs about 64 KB per
+ * contexts at topk = 2048 needs about 32 MB; prefill needs about 64 KB per
  * query row at topk = 2048). The call allocates nothing, on the device or
  * through any library. Every call on one GPU shares that GPU's scratch and
  * the scratch keeps the last call's contents (the kernels initialise what
