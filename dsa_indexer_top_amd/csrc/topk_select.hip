@@ -857,10 +857,11 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams p) {
     }
   }
   // lane weights: heads 32*mb + 8*(r/4) + 4g + r%4, four consecutive heads
-  // per 16-byte load when every row of w starts 16-byte aligned (H % 4 == 0)
+  // per 16-byte load when every row of w starts 16-byte aligned (w itself
+  // 16-byte aligned and H % 4 == 0; w need only be 4-byte aligned)
   float wr[MB][16];
   const float qs = FP8 ? p.q_scale[row] : 1.0f;
-  if ((p.H & 3) == 0) {
+  if ((p.H & 3) == 0 && ((uintptr_t)p.w & 15u) == 0u) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll

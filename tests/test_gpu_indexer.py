@@ -115,6 +115,24 @@ def test_decode_random_bf16(dsa, B, n_k, topk, cfg):
     check_indexer(dsa, inp, topk)
 
 
+def test_decode_weights_4byte_aligned(dsa):
+    """w need only be 4-byte aligned: a w that starts 4 bytes into its
+    allocation (its rows then not 16-byte aligned although H % 4 == 0) gives
+    bitwise the same selection and scores as an aligned copy."""
+    say("decode w at a 4-byte offset")
+    B, n_k, H, k = 3, 5000, 64, 512
+    inp = make_indexer_inputs(B, 1, n_k, H, 128, config=23, w_std=0.125).to("cuda")
+    store = torch.empty(B * H + 1, dtype=torch.float32, device="cuda")
+    w_off = store[1:].view(B, 1, H)
+    w_off.copy_(inp.w)
+    assert w_off.data_ptr() % 16 == 4
+    a = dsa.indexer_scores_topk(inp.q, inp.k, inp.w, k, out_scores=True)
+    b = dsa.indexer_scores_topk(inp.q, inp.k, w_off, k, out_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.idx, b.idx)
+    assert torch.equal(a.scores.view(torch.int32), b.scores.view(torch.int32))
+
+
 def test_decode_exact_integer(dsa):
     say("decode exact")
     inp = make_int_indexer_inputs(2, 1, 3000, 64, 128, seed=13)
