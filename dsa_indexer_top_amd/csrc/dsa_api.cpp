@@ -244,7 +244,7 @@ void indexer_bind_workspace(IndexerParams& p, void* ws) {
 int attn_nsplit(int B, int n_q, int topk) {
   // about 2048 waves over the whole call (the best measured from one decode
   // request to 16K prefill rows), at least one 32-entry chunk per split, at
-  // most 64 splits; a power of two, so that from kAttnGroupWaves splits on
+  // most 64 splits; a power of two, so that from kAttnGroupSplits splits on
   // they fill whole workgroups
   const long rows = (long)B * n_q;
   const int chunks = (topk + 31) / 32;

@@ -128,11 +128,17 @@ size_t attn_workspace_bytes(int B, int n_q, int n_k, int H, int D, int topk);
 int attn_nsplit(int B, int n_q, int topk);
 // Waves per workgroup that merge their splits in LDS, and the partials per
 // row the merge kernel reads for nsplit splits: none for one split (the wave
-// writes the output), one per wave below kAttnGroupWaves splits, one per
-// workgroup of kAttnGroupWaves waves from there on (1 = written directly).
-constexpr int kAttnGroupWaves = 8;
-constexpr int kAttnMaxParts = 8;
-__host__ __device__ inline int attn_nparts(int nsplit) { return nsplit >= kAttnGroupWaves ? nsplit / kAttnGroupWaves : nsplit; }
+// writes the output), one per wave below kAttnGroupSplits splits, one per
+// workgroup from there on: at exactly kAttnGroupSplits splits one workgroup
+// of that many waves writes the output directly (1 partial); from twice that
+// on, workgroups of 4 waves each write one partial (at most 16 per row, at
+// 64 splits), which starts and merges a decode call's waves in smaller groups.
+constexpr int kAttnGroupSplits = 8;
+constexpr int kAttnMaxParts = 16;
+__host__ __device__ inline int attn_group_waves(int nsplit) { return nsplit > kAttnGroupSplits ? 4 : kAttnGroupSplits; }
+__host__ __device__ inline int attn_nparts(int nsplit) {
+  return nsplit >= kAttnGroupSplits ? nsplit / attn_group_waves(nsplit) : nsplit;
+}
 
 // Carves the workspace into the views above.
 void indexer_bind_workspace(IndexerParams& p, void* ws);

@@ -27,9 +27,10 @@
 // Few rows (decode, short prefill chunks) split each row's list over several
 // waves (split-K) so that about 2048 waves share the call. Up to 4 splits
 // each wave writes its (O, max, sum) partial; from 8 splits on, the splits
-// of a workgroup of 8 waves are merged in LDS first, so a row has at most 8
-// partials, or none when one workgroup covers it. A second kernel merges a
-// row's partials by the log-sum-exp rule.
+// of a workgroup are merged in LDS first: at 8 splits one workgroup of 8
+// waves covers the row and writes the output, from 16 splits on workgroups
+// of 4 waves each write one partial (at most 16 per row). A second kernel
+// merges a row's partials by the log-sum-exp rule.
 // A wave with more than one chunk gathers the next chunk's K rows while it
 // computes the current one (its V rows are requested at its start, ahead of
 // its S product); a wave with one chunk gathers K and V together.
@@ -42,8 +43,9 @@ constexpr int kAttnWaves = 4;  // waves per workgroup when every wave is on its 
 constexpr int kAttnChunk = 32;
 
 // Launch forms: one wave per row writing the output; one wave per split
-// writing a partial; workgroups of kAttnGroupWaves split waves that merge in
-// LDS and write the output (one workgroup per row) or one partial each.
+// writing a partial; workgroups of split waves that merge in LDS and write
+// the output (one 8-wave workgroup per row) or one partial each (4-wave
+// workgroups).
 enum AttnMode { kAttnDirect = 0, kAttnSplit = 1, kAttnGroup = 2 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -422,19 +424,23 @@ static void launch_attn_form(const AttnParams& p, hipStream_t s) {
   const int rows = p.B * p.n_q;
   const int ns = p.nsplit;
   const dim3 grid((unsigned)(((long)rows * ns + kAttnWaves - 1) / kAttnWaves));
-  const dim3 ggrid((unsigned)(rows * (ns / kAttnGroupWaves)));
+  const dim3 ggrid((unsigned)(rows * (ns / attn_group_waves(ns))));
   if constexpr (PIPE) {
-    if (ns >= kAttnGroupWaves)
-      hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, kAttnGroup, kAttnGroupWaves>), ggrid, dim3(kAttnGroupWaves * kWave),
-                         0, s, p);
+    if (ns > kAttnGroupSplits)
+      hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, kAttnGroup, 4>), ggrid, dim3(4 * kWave), 0, s, p);
+    else if (ns == kAttnGroupSplits)
+      hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, kAttnGroup, kAttnGroupSplits>), ggrid,
+                         dim3(kAttnGroupSplits * kWave), 0, s, p);
     else if (ns > 1)
       hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, kAttnSplit, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
     else
       hipLaunchKernelGGL((sparse_attn_pipe_kernel<D, kAttnDirect, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
   } else {
-    if (ns >= kAttnGroupWaves)
-      hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnGroup, kAttnGroupWaves>), ggrid, dim3(kAttnGroupWaves * kWave), 0, s,
-                         p);
+    if (ns > kAttnGroupSplits)
+      hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnGroup, 4>), ggrid, dim3(4 * kWave), 0, s, p);
+    else if (ns == kAttnGroupSplits)
+      hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnGroup, kAttnGroupSplits>), ggrid, dim3(kAttnGroupSplits * kWave),
+                         0, s, p);
     else if (ns > 1)
       hipLaunchKernelGGL((sparse_attn_kernel<D, kAttnSplit, kAttnWaves>), grid, dim3(kAttnWaves * kWave), 0, s, p);
     else
@@ -446,7 +452,7 @@ template <int D>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s) {
   const int rows = p.B * p.n_q;
   const int ns = p.nsplit;
-  if (ns < 1 || ns > 64 || (ns >= kAttnGroupWaves && ns % kAttnGroupWaves) || attn_nparts(ns) > kAttnMaxParts)
+  if (ns < 1 || ns > 64 || (ns >= kAttnGroupSplits && ns % attn_group_waves(ns)) || attn_nparts(ns) > kAttnMaxParts)
     return hipErrorInvalidValue;
   // chunks per wave (the kernel's split of the list): prefetch only with more than one
   const int per = ((p.topk + ns - 1) / ns + kAttnChunk - 1) / kAttnChunk;

@@ -171,14 +171,16 @@ def test_workspace_size_is_reported():
     assert dsa.indexer_workspace_size(2, 1, 5000, 64, 128, 2048) > 2 * 5000 * 4
     # attention splits each row over about 2048 / rows waves (at most 64, at
     # least one 32-entry chunk each); partials: one per split below 8 splits,
-    # one per 8-wave workgroup from 8 on, none for one split or one workgroup
+    # none at 8 (one 8-wave workgroup), one per 4-wave workgroup from 16 on
     part = 4 * (128 + 4) * 16
     assert dsa.attn_workspace_size(1, 16384, 16384, 16, 128, 2048) == 0     # one wave per row
     assert dsa.attn_workspace_size(1, 2048, 16384, 16, 128, 2048) == 0      # 2048 rows: one split
     assert dsa.attn_workspace_size(1, 1024, 1024, 16, 128, 2048) == 1024 * 2 * part  # 2 splits
     assert dsa.attn_workspace_size(1, 512, 1024, 16, 128, 2048) == 512 * 4 * part    # 4 splits
     assert dsa.attn_workspace_size(256, 1, 5000, 16, 128, 2048) == 0        # 8 splits: one workgroup
-    assert dsa.attn_workspace_size(2, 1, 5000, 16, 128, 2048) == 2 * 8 * part  # 64 splits: 8 workgroups
+    assert dsa.attn_workspace_size(128, 1, 5000, 16, 128, 2048) == 128 * 4 * part  # 16 splits: 4 workgroups
+    assert dsa.attn_workspace_size(64, 1, 5000, 16, 128, 2048) == 64 * 8 * part    # 32 splits: 8 workgroups
+    assert dsa.attn_workspace_size(2, 1, 5000, 16, 128, 2048) == 2 * 16 * part     # 64 splits: 16 workgroups
     assert dsa.attn_workspace_size(1, 1, 5000, 16, 128, 64) == 2 * part     # two chunks: 2 splits
     assert dsa.attn_workspace_size(4, 1, 5000, 16, 128, 16) == 0            # one chunk
 
