@@ -269,6 +269,37 @@ constexpr int kBucketMaxRun = 256;
 // LDS of the ranking path: the order words, then the bucket counts
 constexpr int bucket_lds_bytes(int bits) { return kMaxC * 8 + (4 << bits); }
 
+// Bucket of an order key over the keys [lo, umax]: a lower bucket holds only
+// larger keys, and equal keys share a bucket. Keys are log-like in the score
+// on either side of zero, so a range on one side is cut into equal key spans,
+// (umax - u) >> shift. A range across zero spans the key bits of every tiny
+// magnitude in between, which would put all scores of ordinary size into a
+// few buckets; there the score itself is cut into equal spans, the rounded
+// (smax - s) * inv (monotone in s, clamped to the last bucket).
+template <int kBuckets>
+struct BucketMap {
+  uint32_t umax;
+  int shift;
+  bool lin;
+  float smax, inv;
+  // lo and hi are the same in every lane; so is the map (scalar registers)
+  __device__ void set(uint32_t lo, uint32_t hi) {
+    lo = uniform_u(lo);
+    umax = uniform_u(hi);
+    shift = (umax - lo) >> __builtin_ctz(kBuckets) ? 32 - __builtin_clz(umax - lo) - __builtin_ctz(kBuckets) : 0;
+    smax = key_score(umax);
+    const float d = smax - key_score(lo);
+    lin = lo < 0x80000000u && umax >= 0x80000000u && d >= 1e-30f && d <= 3e38f;
+    inv = __uint_as_float(uniform_u(__float_as_uint(lin ? (float)kBuckets / d : 0.0f)));
+  }
+  // the range holds more than one bucket's span
+  __device__ bool spread() const { return lin || shift > 0; }
+  __device__ uint32_t operator()(uint32_t u) const {
+    if (lin) return min((uint32_t)((smax - key_score(u)) * inv), (uint32_t)(kBuckets - 1));
+    return (umax - u) >> shift;
+  }
+};
+
 // Entry i = threadIdx.x + e * kFinNTDecode of the list (entries past the
 // list's end are ignored).
 struct BucketEntries {
@@ -322,12 +353,13 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
     umax = max(umax, sh_max[q]);
   }
   uint32_t lo = umin;  // entries with a key >= lo take part
-  int shift = (umax - lo) >> kBucketBits ? 32 - __builtin_clz(umax - lo) - kBucketBits : 0;  // range >> shift < kBuckets
-  if (NARROW && 2 * cnt > 3 * take && shift > 0) {  // uniform
-    __shared__ uint32_t sh_lo;
+  BucketMap<kBuckets> map;
+  map.set(lo, umax);
+  if (NARROW && 2 * cnt > 3 * take && map.spread()) {  // uniform
+    __shared__ uint32_t sh_b;
 #pragma unroll
     for (int e = 0; e < PER; ++e)
-      if (threadIdx.x + e * kFinNTDecode < cnt) atomicAdd(&base[(umax - v.u[e]) >> shift], 1u);
+      if (threadIdx.x + e * kFinNTDecode < cnt) atomicAdd(&base[map(v.u[e])], 1u);
     __syncthreads();
     uint32_t c[BPT], local = 0u;
 #pragma unroll
@@ -339,23 +371,37 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
     uint32_t pre = (uint32_t)block_excl_scan((int)local, scratch, &all);  // its barriers order the reads above
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
-      if (c[q] && pre <= (uint32_t)(take - 1) && (uint32_t)(take - 1) < pre + c[q]) {
-        // the lowest key bucket BPT*t + q spans (umin if that is below it)
-        const uint64_t span = (uint64_t)(BPT * threadIdx.x + q + 1) << shift;
-        sh_lo = span > (uint64_t)(umax - umin) ? umin : (uint32_t)(umax - span + 1u);
-      }
+      if (c[q] && pre <= (uint32_t)(take - 1) && (uint32_t)(take - 1) < pre + c[q]) sh_b = BPT * threadIdx.x + q;
       pre += c[q];
       base[BPT * threadIdx.x + q] = 0u;
     }
     __syncthreads();
-    lo = sh_lo;
-    shift = (umax - lo) >> kBucketBits ? 32 - __builtin_clz(umax - lo) - kBucketBits : 0;
+    const uint32_t bt = sh_b;  // the bucket holding rank take - 1
+    if (!map.lin) {
+      // the lowest key bucket bt spans (umin if that is below it)
+      const uint64_t span = (uint64_t)(bt + 1) << map.shift;
+      lo = span > (uint64_t)(umax - umin) ? umin : (uint32_t)(umax - span + 1u);
+    } else {
+      // the lowest listed key of the buckets up to bt (sh_min is free: the
+      // scan's barriers follow its last read)
+      uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        if (threadIdx.x + e * kFinNTDecode < cnt && map(v.u[e]) <= bt) m = min(m, v.u[e]);
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, d, 64));
+      if (lane == 0) sh_min[w] = m;
+      __syncthreads();
+      lo = sh_min[0];
+#pragma unroll
+      for (int q = 1; q < kSortWaves; ++q) lo = min(lo, sh_min[q]);
+    }
+    map.set(lo, umax);
   }
   uint32_t slot[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e)
-    slot[e] = threadIdx.x + e * kFinNTDecode < cnt && v.u[e] >= lo ? atomicAdd(&base[(umax - v.u[e]) >> shift], 1u)
-                                                                   : 0u;
+    slot[e] = threadIdx.x + e * kFinNTDecode < cnt && v.u[e] >= lo ? atomicAdd(&base[map(v.u[e])], 1u) : 0u;
   __syncthreads();
   uint32_t c[BPT], local = 0u, run = 0u;
 #pragma unroll
@@ -387,7 +433,7 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     if (threadIdx.x + e * kFinNTDecode < cnt && v.u[e] >= lo) {
-      const int s0 = (int)base[(umax - v.u[e]) >> shift];
+      const int s0 = (int)base[map(v.u[e])];
       if (s0 < prefix) word[s0 + slot[e]] = ((uint64_t)v.u[e] << 32) | (uint32_t)~(uint32_t)v.x[e];
     }
   }
@@ -433,7 +479,7 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
 #pragma unroll
     for (int q = 0; q < H; ++q) {
       const bool in = threadIdx.x + q * kFinNTDecode < cnt && v.u[q] >= lo;
-      const uint32_t bk = in ? (umax - v.u[q]) >> shift : 0u;
+      const uint32_t bk = in ? map(v.u[q]) : 0u;
       s0[q] = (int)base[bk];
       len[q] = in && s0[q] < prefix ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : n_in) - s0[q] : 0;
       mine[q] = ((uint64_t)v.u[q] << 32) | (uint32_t)~(uint32_t)v.x[q];
@@ -448,7 +494,7 @@ __device__ bool bucket_rank_topk(const FinalizeParams& p, int r, const BucketEnt
         const int j = threadIdx.x + (g0 + q) * kFinNTDecode;
         const bool in = j < prefix;
         mine[q] = word[in ? j : 0];
-        const uint32_t bk = (umax - (uint32_t)(mine[q] >> 32)) >> shift;
+        const uint32_t bk = map((uint32_t)(mine[q] >> 32));
         s0[q] = (int)base[in ? bk : 0u];
         len[q] = in ? (bk + 1 < (uint32_t)kBuckets ? (int)base[bk + 1] : n_in) - s0[q] : 0;
       }
