@@ -133,14 +133,18 @@ def measured_peaks(torch):
     """Rates of the probes in libdsa_peak.so on this GPU (best of 3 timed
     launches after one untimed): dense MFMA loops in bf16 and fp8 (two
     workgroups of four waves per CU, four independent accumulators per wave),
-    and an HBM copy and read of 2 GiB with 16-byte nontemporal accesses (the
-    best of four grid sizes)."""
+    an HBM copy and read of 2 GiB with 16-byte nontemporal accesses (the
+    best of four grid sizes), and a gather of 256-byte rows (bf16 rows of 128)
+    with the prefill attention's access pattern over tables of the K and V rows
+    of 61440 and of 200000 tokens (the best of three grid sizes)."""
     import ctypes
     lib = ctypes.CDLL(PEAK_LIB)
     lib.dsa_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
     lib.dsa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     lib.dsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dsa_peak_gather.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -183,11 +187,36 @@ def measured_peaks(torch):
         read_best = max(read_best, n / best_ms(rd) / 1e6)
     res["hbm_copy_GBps"] = copy_best
     res["hbm_read_GBps"] = read_best
+    del dst
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12345)
+    res["gather_GBps"] = {}
+    for tokens in (61440, 200000):
+        # the attention's access pattern without its arithmetic: 4096 query
+        # rows t drawn uniformly and taken in increasing order (as the
+        # attention's workgroups go), each listing 2048 keys drawn uniformly
+        # from [0, t], each key's K row (table rows [0, tokens)) and V row
+        # (rows [tokens, 2 tokens)) in turn
+        rows = 2 * tokens
+        t = torch.randint(0, tokens, (4096,), device="cuda", generator=gen).sort().values.unsqueeze(1)
+        key = (torch.rand((4096, 2048), device="cuda", generator=gen) * (t + 1)).long().clamp_(max=tokens - 1)
+        idx = torch.stack((key, key + tokens), dim=-1).flatten().to(torch.int32)
+        ng = idx.numel()
+        del t, key
+        g_best = 0.0
+        for blocks in (2048, 4096, 8192):
+            def ga():
+                if lib.dsa_peak_gather(src.data_ptr(), rows, idx.data_ptr(), ng, blocks, red.data_ptr(), stream) != 0:
+                    raise RuntimeError("dsa_peak_gather failed")
+            g_best = max(g_best, 256 * ng / best_ms(ga) / 1e6)
+        res["gather_GBps"][f"kv_{tokens}_tokens"] = g_best
+        del idx
     res["published"] = {"mfma_bf16_TFLOPs": PEAK_TFLOPS["bf16"], "mfma_fp8_TFLOPs": PEAK_TFLOPS["fp8"],
                         "hbm_GBps": PEAK_HBM_GBS}
     log(f"measured peaks: MFMA bf16 {res['mfma_bf16_TFLOPs']:.0f} TFLOP/s, fp8 {res['mfma_fp8_TFLOPs']:.0f} "
-        f"TFLOP/s; HBM copy {copy_best:.0f} GB/s, read {read_best:.0f} GB/s")
-    del src, dst, red, out
+        f"TFLOP/s; HBM copy {copy_best:.0f} GB/s, read {read_best:.0f} GB/s; row gather "
+        + ", ".join(f"{k} {v:.0f} GB/s" for k, v in res["gather_GBps"].items()))
+    del src, red, out
     torch.cuda.empty_cache()
     return res
 
@@ -730,6 +759,17 @@ def main():
         for part in (extra["decode_attn_B256"], extra["decode_attn_B256"]["cold"]):
             part["attn_gather_frac_of_measured_read"] = part["attn_gather_GBps"] / rd
         extra["quantize_fp8_q_idx"]["frac_of_measured_copy"] = extra["quantize_fp8_q_idx"]["hbm_GBps"] / cp
+        # an S layer is the sparse attention alone: its gathered K and V rows
+        # (min(t + 1, k) of 256 bytes each per query row) against the row-gather
+        # probe over a table of the same size
+        for key, pat, tokens in (("stack_prefill", "freq4", args.stack_L),
+                                 ("stack_prefill_200k", "seeded_quarter_F", L)):
+            s_ms = extra[key][pat]["mean_S_layer_ms"]
+            entries = topk * (tokens - topk) + topk * (topk + 1) // 2 if tokens >= topk else tokens * (tokens + 1) // 2
+            rate = entries * 2 * 256 / s_ms / 1e6
+            probe = peaks["gather_GBps"].get(f"kv_{tokens}_tokens")
+            extra[key]["S_layer_gather_GBps"] = rate
+            extra[key]["S_layer_gather_frac_of_measured_gather"] = rate / probe if probe else None
         result["extra"] = extra
     print(json.dumps(result), flush=True)
 

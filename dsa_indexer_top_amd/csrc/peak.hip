@@ -1,4 +1,4 @@
-// Rate probes (dense MFMA loop, HBM copy and read) for measuring the path's
+// Rate probes (dense MFMA loop, HBM copy and read, row gather) for measuring the path's
 // kernels against peaks taken on the same GPU. Not part of the method.
 #include <hip/hip_runtime.h>
 
@@ -97,6 +97,42 @@ __global__ __launch_bounds__(256) void read16(const u32x4* __restrict__ src, siz
   if (threadIdx.x == 0) out[blockIdx.x] = red[0];
 }
 
+// Row gather: 256-byte rows table[idx[i]], each read by a group of 16 lanes
+// (16 bytes per lane, four rows per wave instruction) and folded (xor) into
+// out[block]. Each group keeps kGatherU rows in flight: their indices are
+// loaded first, then the rows. An index outside [0, rows) reads row rows - 1.
+constexpr int kGatherU = 16;
+
+__global__ __launch_bounds__(256) void gather256(const u32x4* __restrict__ table, size_t rows,
+                                                 const int* __restrict__ idx, size_t n, uint32_t* out) {
+  const int c = threadIdx.x & 15;  // the lane's 16-byte chunk of a row
+  const size_t groups = (size_t)gridDim.x * 16;
+  size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  uint32_t x = 0u;
+  for (; i + (kGatherU - 1) * groups < n; i += kGatherU * groups) {
+    size_t r[kGatherU];
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u) r[u] = min((size_t)(unsigned)idx[i + u * groups], rows - 1);
+    u32x4 v[kGatherU];
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u) v[u] = table[r[u] * 16 + c];
+#pragma unroll
+    for (int u = 0; u < kGatherU; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n; i += groups) {
+    const u32x4 a = table[min((size_t)(unsigned)idx[i], rows - 1) * 16 + c];
+    x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int d = 128; d >= 1; d >>= 1) {
+    if ((int)threadIdx.x < d) red[threadIdx.x] ^= red[threadIdx.x + d];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+}
+
 int launched() { return hipGetLastError() == hipSuccess ? 0 : 2; }
 
 }  // namespace
@@ -123,5 +159,14 @@ extern "C" int dsa_peak_copy(const void* src, void* dst, size_t bytes, int block
 extern "C" int dsa_peak_read(const void* src, size_t bytes, int blocks, uint32_t* out, void* stream) {
   if (!src || !out || bytes % 16 || blocks < 1 || (uintptr_t)src % 16) return 1;
   hipLaunchKernelGGL(read16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, bytes / 16, out);
+  return launched();
+}
+
+extern "C" int dsa_peak_gather(const void* table, size_t rows, const int32_t* idx, size_t n, int blocks, uint32_t* out,
+                               void* stream) {
+  if (!table || !idx || !out || rows < 1 || n < 1 || blocks < 1 || (uintptr_t)table % 16 || (uintptr_t)idx % 4)
+    return 1;
+  hipLaunchKernelGGL(gather256, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)table, rows,
+                     (const int*)idx, n, out);
   return launched();
 }

@@ -3,7 +3,8 @@
  *
  * None of these is a step of the method: they put a number next to the
  * published peaks (dense MFMA 2.5 PFLOP/s bf16, 5.0 PFLOP/s fp8; HBM
- * 8 TB/s) so that the kernels' fractions can be stated against both.
+ * 8 TB/s) so that the kernels' fractions can be stated against both, and a
+ * random row gather next to the sparse attention's.
  * All calls are asynchronous on the given HIP stream (NULL: the default
  * stream), take device pointers the caller owns, allocate nothing and return
  * 0 on success, 1 for an invalid argument, 2 for a launch error.
@@ -36,6 +37,16 @@ int dsa_peak_copy(const void* src, void* dst, size_t bytes, int blocks, void* st
  * (nontemporal, sixteen in flight per thread) and folded (xor) into
  * out[block] (blocks words), so the loads are kept. */
 int dsa_peak_read(const void* src, size_t bytes, int blocks, uint32_t* out, void* stream);
+
+/* Row gather: for i < n, the 256-byte row table[idx[i]] of a table of `rows`
+ * rows (16-byte aligned) is read and folded (xor) into out[block] (blocks
+ * words), sixteen lanes per row and sixteen rows in flight per lane group,
+ * grid-stride over `blocks` workgroups of 256 threads. An index outside
+ * [0, rows) reads the last row. Moves 256 * n bytes of rows plus 4 * n of
+ * indices: the rate an index-driven gather of bf16 rows of 128 values (the
+ * sparse attention's K and V rows) reaches from wherever the table sits. */
+int dsa_peak_gather(const void* table, size_t rows, const int32_t* idx, size_t n, int blocks, uint32_t* out,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,7 @@ def test_peak_probe_library_exports():
     path = os.path.join(ROOT, "dsa_indexer_top_amd", "libdsa_peak.so")
     plib = ctypes.CDLL(path)
     declared = _declared_functions("dsa_peak.h")
-    assert declared == ["dsa_peak_copy", "dsa_peak_mfma", "dsa_peak_read"]
+    assert declared == ["dsa_peak_copy", "dsa_peak_gather", "dsa_peak_mfma", "dsa_peak_read"]
     for name in declared:
         assert hasattr(plib, name), name
     plib.dsa_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,

@@ -1,6 +1,6 @@
 """The rate probes the benchmark measures peaks with compute what they claim:
-the copy and the read touch every byte, the MFMA loop runs to completion with
-the same result in every workgroup."""
+the copy and the read touch every byte, the gather reads every listed row,
+the MFMA loop runs to completion with the same result in every workgroup."""
 import ctypes
 import os
 
@@ -21,6 +21,8 @@ def plib():
                                   ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
     lib.dsa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     lib.dsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dsa_peak_gather.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -55,3 +57,23 @@ def test_mfma_loop(plib, dtype):
     o = out.view(blocks, 256)
     assert torch.isfinite(o).all() and (o != 0).any()
     assert torch.equal(o, o[0:1].expand_as(o))
+
+
+def test_gather(plib):
+    say("peak probes: gather")
+    s = torch.cuda.current_stream().cuda_stream
+    rows, n, blocks = 1000, 100003, 32     # n: a ragged tail after the 8-row rounds
+    g = torch.Generator().manual_seed(7)
+    table = torch.randint(-2**31, 2**31 - 1, (rows, 64), dtype=torch.int32, generator=g)
+    idx = torch.randint(0, rows, (n,), dtype=torch.int32, generator=g)
+    idx[5], idx[n - 1] = -1, rows + 7       # out of range: read the last row
+    red = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    td, idd = table.cuda(), idx.cuda()
+    assert plib.dsa_peak_gather(td.data_ptr(), rows, idd.data_ptr(), n, blocks, red.data_ptr(), s) == 0
+    assert plib.dsa_peak_gather(td.data_ptr(), 0, idd.data_ptr(), n, blocks, red.data_ptr(), s) == 1
+    torch.cuda.synchronize()
+    folded = np.bitwise_xor.reduce(table.numpy().view(np.uint32), axis=1)
+    i = idx.numpy()
+    want = int(np.bitwise_xor.reduce(folded[np.where((i < 0) | (i >= rows), rows - 1, i)]))
+    got = int(np.bitwise_xor.reduce(red.cpu().numpy().view(np.uint32)))
+    assert got == want
