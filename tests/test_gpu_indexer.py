@@ -65,6 +65,29 @@ def test_prefill_k2048_compaction(dsa):
     check_indexer(dsa, inp, 2048, rows=sorted(set(int(r) for r in rows)))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_prefill_scores_across_zero_wide_range(dsa, dtype):
+    """Exact inputs whose keys are scaled by 2^-12, except every 61st by 2^5:
+    every row's scores take both signs, almost all of them tiny, a few large.
+    Rows holding every causal key bucket a range across zero (by the score,
+    not the key bits), whose middle bucket then overflows: the ranking must
+    fall back to the exact select. Rows past 1.5 k candidates go through the
+    narrowing pre-pass first. Scores stay exact: each one's terms share the
+    key's scale."""
+    say(f"prefill {dtype} scores across zero, wide range")
+    L = 4000
+    inp = make_int_indexer_inputs(1, L, L, 16, 64, seed=21, dtype=dtype)
+    scale = torch.full((L,), 2.0 ** -12)
+    scale[::61] = 2.0 ** 5
+    if dtype == "bf16":
+        inp.k = (inp.k.float() * scale[None, :, None]).to(torch.bfloat16)
+    else:
+        inp.k_scale = (inp.k_scale * scale[None, :]).contiguous()
+    rows = [0, 1, 60, 61, 62, 2046, 2047, 2048, 3070, 3071, 3072, 3073, L - 1]
+    rows += list(np.random.default_rng(3).choice(L, 12, replace=False))
+    check_indexer(dsa, inp, 2048, rows=sorted(set(int(r) for r in rows)), exact=True)
+
+
 def test_prefill_all_ties(dsa):
     """q = 0: every score is 0, so each row must list its first min(k, t+1)
     tokens in index order (tie rule through many compactions)."""
