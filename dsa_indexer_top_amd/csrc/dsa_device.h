@@ -24,6 +24,13 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// score_key of a score that is not -0.0: a negative score flips every bit, a
+// positive one only the sign bit.
+__device__ __forceinline__ uint32_t score_key_nz(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+
 __device__ __forceinline__ float key_score(uint32_t u) {
   uint32_t b = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
   return __uint_as_float(b);

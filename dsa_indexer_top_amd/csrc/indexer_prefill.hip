@@ -547,7 +547,9 @@ void indexer_prefill_kernel(IndexerParams p) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pend_p0), __float_as_uint(pend_p1),
                                                      false, false);
     float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if constexpr (FP8) score *= pend_ksc;
+    // never -0 after this (fp8: fma with +0; bf16: + 0), so the commit can
+    // take the order key without its -0 case
+    score = FP8 ? __builtin_fmaf(score, pend_ksc, 0.0f) : score + 0.0f;
     f_score = score;
     asm volatile("" : "+v"(f_score));
   };
@@ -555,7 +557,9 @@ void indexer_prefill_kernel(IndexerParams p) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pend_p0), __float_as_uint(pend_p1),
                                                      false, false);
     float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if constexpr (FP8) score *= pend_ksc;
+    // never -0 after this (fp8: fma with +0; bf16: + 0), so the commit can
+    // take the order key without its -0 case
+    score = FP8 ? __builtin_fmaf(score, pend_ksc, 0.0f) : score + 0.0f;
     f_score_a = score;
     asm volatile("" : "+v"(f_score_a));
   };
@@ -569,19 +573,22 @@ void indexer_prefill_kernel(IndexerParams p) {
       if (valid) p.dump[row * (size_t)p.n_k + key] = canon_zero(f_score);
     }
     const bool take_a = valid_a && f_score_a > theta_f, take = valid && f_score > theta_f;
-    const uint64_t am_a = ballot(take_a), am = ballot(take);
+    // a ballot of one compare is that compare's lane mask (a ballot of the
+    // combined condition would go through a VGPR)
+    const uint64_t am_a = ballot(valid_a) & ballot(f_score_a > theta_f);
+    const uint64_t am = ballot(valid) & ballot(f_score > theta_f);
     if (am_a | am) {
       // list order = key order: the previous tile's keys first
       // 32-bit byte offsets from the row's (scalar) list bases: no 64-bit address math
       if (take_a) {
         const uint32_t off = 4u * (uint32_t)(cnt + mbcnt(am_a));
-        *(uint32_t*)((unsigned char*)ckey + off) = score_key(f_score_a);
+        *(uint32_t*)((unsigned char*)ckey + off) = score_key_nz(f_score_a);
         *(int32_t*)((unsigned char*)cidx + off) = key_a;
       }
       const int cnt_b = cnt + popc64(am_a);
       if (take) {
         const uint32_t off = 4u * (uint32_t)(cnt_b + mbcnt(am));
-        *(uint32_t*)((unsigned char*)ckey + off) = score_key(f_score);
+        *(uint32_t*)((unsigned char*)ckey + off) = score_key_nz(f_score);
         *(int32_t*)((unsigned char*)cidx + off) = key;
       }
       cnt = cnt_b + popc64(am);
@@ -649,7 +656,8 @@ void indexer_prefill_kernel(IndexerParams p) {
       // unconditional loads, clamped into the row's n_k scales (no exec-mask
       // branch); keys past kend get scale 0
       const int i0 = base + lane, i1 = base + kTileKeys + lane;
-      const float s0 = kscale[min(i0, p.n_k - 1)], s1 = kscale[min(i1, p.n_k - 1)];
+      const float s0 = *(const float*)((const char*)kscale + 4u * (uint32_t)min(i0, p.n_k - 1));
+      const float s1 = *(const float*)((const char*)kscale + 4u * (uint32_t)min(i1, p.n_k - 1));
       ksc0 = (mine && i0 < kend) ? s0 : 0.0f;
       ksc1 = (mine && i1 < kend) ? s1 : 0.0f;
     }
